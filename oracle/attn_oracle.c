@@ -1,0 +1,279 @@
+/*
+ * Attention-forward oracle: TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU implementation in double precision of what the GPU path
+ * computes.  Only the tests, the package smoke check and the bench's CPU
+ * baseline may load it; the product library never links or calls it, and it
+ * shares no code, header or table with the GPU kernels.
+ *
+ * What is computed (LuisaCompute "Attention execution mapping" review,
+ * section 1, the attention fixture paragraph): bottom-right causal
+ * grouped-query attention.  Query head h reads kv-head h / (Hq/Hkv) (integer
+ * division, contiguous groups); key k is legal for query row q when
+ * k <= q + K - Q.  Readings where the pages are silent (each listed in the
+ * design notes):
+ *   - per-sequence length K_b replaces K in that offset, p(q) = q + K_b - Q,
+ *     and only keys k < K_b exist (Laya "Fast backends", "Numerics": int32
+ *     lengths, unequal lengths, empty sequences);
+ *   - a sliding window W > 0 keeps the W keys p-W < k <= p (diagonal included);
+ *   - a row with no legal key gets O = 0 and LSE = -inf (finite padded rows);
+ *   - LSE is the natural log of the sum of exp(scale * q.k) over legal keys.
+ * The softmax is written out in full: scores, their maximum, the exponentials,
+ * their sum, the normalised weights and the weighted sum of V rows.  There is
+ * no blocking and no online rescaling.
+ *
+ * Inputs are read element by element from bf16 (dtype 0, widened exactly) or
+ * fp32 (dtype 1) storage and every operation is done in double.  Row strides
+ * (ldq, ldk, ldv, ldo) are in elements, so tests can embed V and O in wider
+ * rows and check that columns beyond Dv are never read or written.
+ *
+ * ORACLE_MUTANT (compile-time, tests only) plants one known mistake so the
+ * pin tests can show they would catch it; the default build defines none.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+static double load_elem(const void* base, int dtype, int64_t i) {
+  if (dtype == 0) {
+    uint16_t h = ((const uint16_t*)base)[i];
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  return (double)((const float*)base)[i];
+}
+
+/* The legality predicate of one (row, key) pair. */
+static int legal(int64_t k, int64_t p, int64_t Kb, int window) {
+#if ORACLE_MUTANT == 3 /* causal diagonal off by one */
+  if (!(k <= p + 1)) return 0;
+#else
+  if (!(k <= p)) return 0;
+#endif
+  if (!(k >= 0 && k < Kb)) return 0;
+#if ORACLE_MUTANT == 5 /* window one key too wide */
+  if (window > 0 && !(k >= p - window)) return 0;
+#else
+  if (window > 0 && !(k > p - window)) return 0;
+#endif
+  return 1;
+}
+
+/*
+ * Scores of one row (b, h, q) over all K key slots: scores[k] = scale * q.k for
+ * legal keys, is_legal[k] marks them.  Returns the number of legal keys.
+ */
+static int64_t row_scores(const void* q, const void* k, int dtype, int Hq, int Hkv, int Q, int K, int D,
+                          const int32_t* seqlens, int window, double scale, int64_t ldq, int64_t ldk, int b, int h,
+                          int qi, double* scores, unsigned char* is_legal) {
+#if ORACLE_MUTANT == 2 /* wrong GQA map: modulo instead of integer division */
+  int kh = h % Hkv;
+#else
+  int kh = h / (Hq / Hkv);
+#endif
+#if ORACLE_MUTANT == 10 /* per-sequence lengths ignored */
+  int64_t Kb = K;
+#else
+  int64_t Kb = seqlens ? seqlens[b] : K;
+#endif
+#if ORACLE_MUTANT == 4 /* top-left instead of bottom-right alignment */
+  int64_t p = qi;
+#else
+  int64_t p = (int64_t)qi + Kb - Q;
+#endif
+  const int64_t qrow = (((int64_t)b * Hq + h) * Q + qi) * ldq;
+  const int64_t kbase = ((int64_t)b * Hkv + kh) * (int64_t)K;
+  int64_t n_legal = 0;
+  for (int64_t kk = 0; kk < K; ++kk) {
+    is_legal[kk] = (unsigned char)legal(kk, p, Kb, window);
+    if (!is_legal[kk]) continue;
+    ++n_legal;
+    double dot = 0.0;
+#if ORACLE_MUTANT == 11 /* last channel of the dot product dropped */
+    for (int d = 0; d < D - 1; ++d)
+#else
+    for (int d = 0; d < D; ++d)
+#endif
+      dot += load_elem(q, dtype, qrow + d) * load_elem(k, dtype, (kbase + kk) * ldk + d);
+#if ORACLE_MUTANT == 1 /* scale dropped */
+    scores[kk] = dot;
+#elif ORACLE_MUTANT == 12 /* sign error */
+    scores[kk] = -scale * dot;
+#else
+    scores[kk] = scale * dot;
+#endif
+  }
+  return n_legal;
+}
+
+/* One output row (b, h, q): writes o_row[0..Dv) and *lse_out. */
+static void oracle_row(const void* q, const void* k, const void* v, int dtype, int Hq, int Hkv, int Q, int K,
+                       int D, int Dv, const int32_t* seqlens, int window, double scale, int64_t ldq, int64_t ldk,
+                       int64_t ldv, int b, int h, int qi, double* o_row, double* lse_out, double* scores,
+                       unsigned char* is_legal) {
+  int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, scale, ldq, ldk, b, h, qi, scores,
+                               is_legal);
+  if (n_legal == 0) {
+    for (int j = 0; j < Dv; ++j) o_row[j] = 0.0;
+    *lse_out = -INFINITY;
+    return;
+  }
+  const int kh = h / (Hq / Hkv);
+  const int64_t kbase = ((int64_t)b * Hkv + kh) * (int64_t)K;
+  double m = -INFINITY;
+  for (int64_t kk = 0; kk < K; ++kk)
+    if (is_legal[kk] && scores[kk] > m) m = scores[kk];
+  double l = 0.0;
+  for (int64_t kk = 0; kk < K; ++kk)
+    if (is_legal[kk]) l += exp(scores[kk] - m);
+  for (int j = 0; j < Dv; ++j) {
+    double acc = 0.0;
+    for (int64_t kk = 0; kk < K; ++kk) {
+      if (!is_legal[kk]) continue;
+#if ORACLE_MUTANT == 7 /* V indexed as if transposed: channel and key swapped */
+      double vv = load_elem(v, dtype, (kbase + (j % K)) * ldv + (kk % Dv));
+#else
+      double vv = load_elem(v, dtype, (kbase + kk) * ldv + j);
+#endif
+#if ORACLE_MUTANT == 9 /* weights not normalised by the sum */
+      acc += exp(scores[kk] - m) * vv;
+#else
+      acc += exp(scores[kk] - m) / l * vv;
+#endif
+    }
+    o_row[j] = acc;
+  }
+#if ORACLE_MUTANT == 6 /* row max left out of the log-sum-exp */
+  *lse_out = log(l);
+#elif ORACLE_MUTANT == 13 /* base-2 log */
+  *lse_out = (m + log(l)) / log(2.0);
+#else
+  *lse_out = m + log(l);
+#endif
+}
+
+static int check_args(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return -1;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return -1;
+  if (seqlens)
+    for (int b = 0; b < B; ++b)
+      if (seqlens[b] < 0 || seqlens[b] > K) return -2;
+  return 0;
+}
+
+/*
+ * Full problem: o[((b*Hq+h)*Q+q)*ldo + j], lse[(b*Hq+h)*Q+q].
+ * Returns 0, -1 for bad sizes, -2 for a length outside [0, K], -3 on OOM.
+ */
+int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, double* o, double* lse, int B, int Hq,
+                    int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window, double scale,
+                    int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int threads) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens);
+  if (rc) return rc;
+  const int64_t rows = (int64_t)B * Hq * Q;
+  int bad = 0;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    unsigned char* lg = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
+    /* Every thread reaches the work-sharing loop; a thread without buffers only flags. */
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!scores || !lg) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int qi = (int)(r % Q);
+      int h = (int)((r / Q) % Hq);
+      int b = (int)(r / ((int64_t)Q * Hq));
+      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, scale, ldq, ldk, ldv, b, h, qi,
+                 o + r * ldo, lse + r, scores, lg);
+    }
+    free(scores);
+    free(lg);
+  }
+  return bad ? -3 : 0;
+}
+
+/*
+ * Selected rows only: rows[i] is the flat row index (b*Hq+h)*Q+q; the result
+ * for rows[i] goes to o[i*Dv ...] and lse[i].  Used to check sampled outputs
+ * of workloads too large to compute in full on the host.
+ */
+int oracle_attn_fwd_rows(const void* q, const void* k, const void* v, int dtype, double* o, double* lse, int B,
+                         int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window,
+                         double scale, const int64_t* rows, int64_t nrows, int threads) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens);
+  if (rc) return rc;
+  const int64_t total = (int64_t)B * Hq * Q;
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= total) return -1;
+  int bad = 0;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    unsigned char* lg = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+      if (!scores || !lg) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int64_t r = rows[i];
+      int qi = (int)(r % Q);
+      int h = (int)((r / Q) % Hq);
+      int b = (int)(r / ((int64_t)Q * Hq));
+      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, scale, D, D, Dv, b, h, qi,
+                 o + i * Dv, lse + i, scores, lg);
+    }
+    free(scores);
+    free(lg);
+  }
+  return bad ? -3 : 0;
+}
+
+/*
+ * The normalised weights P[k] of one row (0 for keys that are not legal),
+ * so tests can check that they sum to one.  Returns the number of legal keys,
+ * or a negative code as oracle_attn_fwd does.
+ */
+int64_t oracle_attn_probs(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int Q, int K, int D,
+                          const int32_t* seqlens, int window, double scale, int b, int h, int qi, double* p_out) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, 1, seqlens);
+  if (rc) return rc;
+  double* scores = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  unsigned char* lg = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
+  if (!scores || !lg) {
+    free(scores);
+    free(lg);
+    return -3;
+  }
+  int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, scale, D, D, b, h, qi, scores, lg);
+  double m = -INFINITY;
+  for (int64_t kk = 0; kk < K; ++kk)
+    if (lg[kk] && scores[kk] > m) m = scores[kk];
+  double l = 0.0;
+  for (int64_t kk = 0; kk < K; ++kk)
+    if (lg[kk]) l += exp(scores[kk] - m);
+  for (int64_t kk = 0; kk < K; ++kk) {
+    p_out[kk] = 0.0;
+    if (!lg[kk]) continue;
+#if ORACLE_MUTANT == 9
+    p_out[kk] = exp(scores[kk] - m);
+#else
+    p_out[kk] = exp(scores[kk] - m) / l;
+#endif
+  }
+  free(scores);
+  free(lg);
+  return n_legal;
+}

@@ -1,0 +1,50 @@
+"""Build the fp64 CPU oracle (plain C, OpenMP) -- test infrastructure only.
+
+`build()` compiles oracle/attn_oracle.c into oracle/libattn_oracle.so with gcc.
+`build_mutant(n, outdir)` compiles the same source with ORACLE_MUTANT=n, a
+variant with one planted mistake that the pin tests must reject.
+No fast-math: the oracle keeps IEEE double semantics and source order.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "attn_oracle.c")
+LIB = os.path.join(HERE, "libattn_oracle.so")
+CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra", "-fno-fast-math"]
+
+# Planted mistakes, each a one-line change under ORACLE_MUTANT in attn_oracle.c.
+MUTANTS = {
+    1: "scale dropped",
+    2: "GQA map h % Hkv instead of h / (Hq/Hkv)",
+    3: "causal diagonal off by one",
+    4: "top-left instead of bottom-right alignment",
+    5: "window one key too wide",
+    6: "row max left out of the LSE",
+    7: "V operand indexed transposed",
+    9: "weights not normalised",
+    10: "per-sequence lengths ignored",
+    11: "last channel of the dot product dropped",
+    12: "score sign flipped",
+    13: "LSE in base 2",
+}
+
+
+def _compile(out, defines=()):
+    tmp = out + ".tmp"
+    cmd = ["gcc", *CFLAGS, *[f"-D{d}" for d in defines], "-o", tmp, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    return _compile(LIB)
+
+
+def build_mutant(n: int, outdir: str) -> str:
+    return _compile(os.path.join(outdir, f"libattn_oracle_m{n}.so"), [f"ORACLE_MUTANT={n}"])
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,316 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each pin takes an oracle object (oracle.attn_oracle.Oracle) and raises
+AssertionError when the oracle disagrees with:
+  - hand-derived worked examples (tests/golden/worked_examples.json),
+  - textbook causal attention as computed by torch's scaled_dot_product_attention
+    in float64 on the CPU (a library routine),
+  - closed forms (uniform V, a single legal key, zero scale),
+  - invariants (shift of K along a fixed direction, weights summing to one,
+    split-and-merge by log-sum-exp, GQA equal to MHA on repeated heads,
+    padding never read, V/O columns beyond Dv never touched).
+The definition pinned is the attention fixture of the LuisaCompute "Attention
+execution mapping" review, section 1 (bottom-right causal GQA, kv-head
+h/(Hq/Hkv), legal keys k <= q + K - Q, online state carried across KV blocks),
+with the per-sequence-length and window readings stated in the design notes.
+
+The mutation test runs INDEPENDENT_PINS on oracle builds with one planted
+mistake each and requires every build to fail at least one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f32(rng, shape, scale=1.0):
+    return (rng.standard_normal(shape) * scale).astype(np.float32)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    ninf_a, ninf_b = np.isneginf(a), np.isneginf(b)
+    assert np.array_equal(ninf_a, ninf_b), f"{what}: -inf pattern differs"
+    fa, fb = a[~ninf_a], b[~ninf_b]
+    assert np.all(np.isfinite(fa)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(fa - fb))) if fa.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _sdpa_causal_square(q, k, v, scale):
+    """Textbook lower-triangular causal attention (Q == K) via torch, float64, CPU.
+    Returns (o, lse) with kv heads repeated over their query groups."""
+    tq = torch.from_numpy(q.astype(np.float64))
+    tk = torch.from_numpy(k.astype(np.float64))
+    tv = torch.from_numpy(v.astype(np.float64))
+    g = tq.shape[1] // tk.shape[1]
+    tk = tk.repeat_interleave(g, dim=1)
+    tv = tv.repeat_interleave(g, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+    n = tq.shape[2]
+    s = scale * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+    tri = torch.ones(n, n, dtype=torch.bool).tril()
+    s = s.masked_fill(~tri, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+# ---------------------------------------------------------------- worked examples
+def pin_worked_examples(orc):
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        ex = json.load(f)
+    q = np.array(ex["q"], dtype=np.float32)
+    k = np.array(ex["k"], dtype=np.float32)
+    v = np.array(ex["v"], dtype=np.float32)
+    assert ex["scale"] == "ln3"
+    for case in ex["cases"]:
+        sl = None if case["seqlens"] is None else np.array(case["seqlens"], dtype=np.int32)
+        o, lse = orc.fwd(q, k, v, seqlens=sl, window=case["window"], scale=math.log(3.0))
+        want_o = np.array([[[[float(Fraction(x)) for x in row] for row in head] for head in bat]
+                           for bat in case["o"]])
+        want_lse = np.array([[[(-math.inf if x == "-inf" else math.log(Fraction(x[3:]))) for x in head]
+                              for head in bat] for bat in case["lse"]])
+        _close(o, want_o, 1e-12, f"worked example {case['name']} O")
+        _close(lse, want_lse, 1e-12, f"worked example {case['name']} LSE")
+
+
+# ---------------------------------------------------------------- textbook / library
+def pin_textbook_causal(orc):
+    rng = np.random.default_rng(11)
+    for (B, Hq, Hkv, N, D, Dv) in [(2, 4, 2, 37, 16, 24), (1, 3, 3, 20, 8, 8), (1, 4, 1, 33, 32, 16)]:
+        q, k, v = _f32(rng, (B, Hq, N, D)), _f32(rng, (B, Hkv, N, D)), _f32(rng, (B, Hkv, N, Dv))
+        scale = 1.0 / math.sqrt(D)
+        o, lse = orc.fwd(q, k, v, scale=scale)
+        ro, rl = _sdpa_causal_square(q, k, v, scale)
+        _close(o, ro, 1e-12, f"textbook causal O {B,Hq,Hkv,N,D,Dv}")
+        _close(lse, rl, 1e-12, f"textbook causal LSE {B,Hq,Hkv,N,D,Dv}")
+
+
+def pin_bottom_right(orc):
+    """Q < K rows are the last Q rows of the square causal problem (decode included)."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, K, D, Dv = 1, 4, 2, 29, 16, 8
+    qf, k, v = _f32(rng, (B, Hq, K, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    scale = 0.37
+    ro, rl = _sdpa_causal_square(qf, k, v, scale)
+    for Q in (1, 2, 5, 17):
+        q = np.ascontiguousarray(qf[:, :, K - Q:, :])
+        o, lse = orc.fwd(q, k, v, scale=scale)
+        _close(o, ro[:, :, K - Q:, :], 1e-12, f"bottom-right Q={Q} O")
+        _close(lse, rl[:, :, K - Q:], 1e-12, f"bottom-right Q={Q} LSE")
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_uniform_v(orc):
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 4, 2, 7, 19, 16, 12
+    q, k = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D))
+    row = _f32(rng, (B, Hkv, 1, Dv))
+    v = np.ascontiguousarray(np.broadcast_to(row, (B, Hkv, K, Dv)))
+    for window, sl in [(0, None), (3, None), (0, np.array([19, 4], np.int32))]:
+        o, lse = orc.fwd(q, k, v, seqlens=sl, window=window)
+        want = np.repeat(np.repeat(row.astype(np.float64), Hq // Hkv, axis=1), Q, axis=2)
+        has = np.isfinite(lse)
+        assert has.any()
+        _close(o[has], want[has], 1e-12, "uniform V gives V")
+
+
+def pin_single_key(orc):
+    """Window 1, or K_b = 1 at the last row: O is that key's V row and LSE its score."""
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, Q, K, D, Dv = 1, 4, 2, 6, 11, 16, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    scale = 0.5
+    o, lse = orc.fwd(q, k, v, window=1, scale=scale)
+    for h in range(Hq):
+        kh = h // (Hq // Hkv)
+        for i in range(Q):
+            p = i + K - Q
+            _close(o[0, h, i], v[0, kh, p], 1e-12, "window 1 O")
+            want = scale * float(np.dot(q[0, h, i].astype(np.float64), k[0, kh, p].astype(np.float64)))
+            _close(lse[0, h, i], want, 1e-12, "window 1 LSE")
+    o, lse = orc.fwd(q, k, v, seqlens=np.array([1], np.int32), scale=scale)
+    for h in range(Hq):
+        kh = h // (Hq // Hkv)
+        _close(o[0, h, Q - 1], v[0, kh, 0], 1e-12, "K_b = 1 O")
+        want = scale * float(np.dot(q[0, h, Q - 1].astype(np.float64), k[0, kh, 0].astype(np.float64)))
+        _close(lse[0, h, Q - 1], want, 1e-12, "K_b = 1 LSE")
+
+
+def pin_scale_zero(orc):
+    """scale 0: uniform weights over the legal keys, so O is their mean and LSE ln(count)."""
+    rng = np.random.default_rng(15)
+    B, Hq, Hkv, N, D, Dv = 1, 2, 1, 23, 8, 8
+    q, k, v = _f32(rng, (B, Hq, N, D)), _f32(rng, (B, Hkv, N, D)), _f32(rng, (B, Hkv, N, Dv))
+    vd = v.astype(np.float64)
+    for window in (0, 5):
+        o, lse = orc.fwd(q, k, v, window=window, scale=0.0)
+        for i in range(N):
+            lo = 0 if window <= 0 else max(0, i - window + 1)
+            want = vd[0, 0, lo:i + 1].mean(axis=0)
+            for h in range(Hq):
+                _close(o[0, h, i], want, 1e-12, f"scale 0 O (window {window})")
+                _close(lse[0, h, i], math.log(i + 1 - lo), 1e-12, f"scale 0 LSE (window {window})")
+
+
+def pin_empty_rows(orc):
+    rng = np.random.default_rng(16)
+    B, Hq, Hkv, Q, K, D, Dv = 3, 2, 1, 9, 6, 8, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    sl = np.array([0, 6, 2], np.int32)
+    o, lse = orc.fwd(q, k, v, seqlens=sl)
+    for b in range(B):
+        for i in range(Q):
+            empty = (i + sl[b] - Q) < 0   # no key at or before the row's position
+            if empty:
+                assert np.all(o[b, :, i] == 0.0), "empty row O must be 0"
+                assert np.all(np.isneginf(lse[b, :, i])), "empty row LSE must be -inf"
+            else:
+                assert np.all(np.isfinite(lse[b, :, i])), "row with keys must have finite LSE"
+    assert np.all(np.isfinite(o))
+
+
+# ---------------------------------------------------------------- invariants
+def pin_shift_invariance(orc):
+    """K' = K + 1 u^T: weights unchanged, LSE moves by scale * q.u (exact inputs on a 1/8 grid)."""
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, Q, K, D, Dv = 1, 4, 2, 5, 13, 16, 8
+    grid = lambda shape: (rng.integers(-8, 9, size=shape) / 8.0).astype(np.float32)
+    q, k, v = grid((B, Hq, Q, D)), grid((B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    u = grid((B, Hkv, 1, D))
+    u[..., -1] = 0.75
+    k2 = np.ascontiguousarray(k + u)
+    scale = 0.25
+    o1, l1 = orc.fwd(q, k, v, scale=scale, window=4)
+    o2, l2 = orc.fwd(q, k2, v, scale=scale, window=4)
+    _close(o2, o1, 1e-12, "shift invariance O")
+    g = Hq // Hkv
+    ur = np.repeat(u.astype(np.float64), g, axis=1)[:, :, 0, :]
+    shift = scale * np.einsum("bhqd,bhd->bhq", q.astype(np.float64), ur)
+    _close(l2, l1 + shift, 1e-12, "shift invariance LSE")
+
+
+def pin_probs_sum_to_one(orc):
+    rng = np.random.default_rng(18)
+    B, Hq, Hkv, Q, K, D = 2, 4, 2, 8, 21, 16
+    q, k = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D))
+    sl = np.array([21, 5], np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Q):
+                p, n = orc.probs(q, k, b, h, i, seqlens=sl, window=6)
+                assert np.all(p >= 0.0)
+                assert np.count_nonzero(p) <= n
+                if n:
+                    assert abs(math.fsum(p) - 1.0) <= 1e-13, "weights must sum to 1"
+                else:
+                    assert not p.any()
+
+
+def pin_split_merge(orc):
+    """Attention over [0,K) equals the log-sum-exp merge of [0,s) and [s,K)."""
+    rng = np.random.default_rng(19)
+    Hq, Hkv, K, D, Dv = 2, 1, 40, 16, 8
+    q, k, v = _f32(rng, (1, Hq, 1, D)), _f32(rng, (1, Hkv, K, D)), _f32(rng, (1, Hkv, K, Dv))
+    of, lf = orc.fwd(q, k, v)
+    for s in (1, 17, 39):
+        o1, l1 = orc.fwd(q, np.ascontiguousarray(k[:, :, :s]), np.ascontiguousarray(v[:, :, :s]))
+        o2, l2 = orc.fwd(q, np.ascontiguousarray(k[:, :, s:]), np.ascontiguousarray(v[:, :, s:]))
+        m = np.maximum(l1, l2)
+        w1, w2 = np.exp(l1 - m), np.exp(l2 - m)
+        om = (w1[..., None] * o1 + w2[..., None] * o2) / (w1 + w2)[..., None]
+        lm = m + np.log(w1 + w2)
+        _close(om, of, 1e-12, f"split-merge O at {s}")
+        _close(lm, lf, 1e-12, f"split-merge LSE at {s}")
+
+
+def pin_gqa_expand(orc):
+    rng = np.random.default_rng(20)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 8, 2, 6, 15, 16, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    sl = np.array([15, 9], np.int32)
+    o, lse = orc.fwd(q, k, v, seqlens=sl, window=7)
+    g = Hq // Hkv
+    ke, ve = np.ascontiguousarray(np.repeat(k, g, axis=1)), np.ascontiguousarray(np.repeat(v, g, axis=1))
+    o2, l2 = orc.fwd(q, ke, ve, seqlens=sl, window=7)
+    _close(o, o2, 0.0, "GQA equals MHA on repeated kv heads (O)")
+    _close(lse, l2, 0.0, "GQA equals MHA on repeated kv heads (LSE)")
+
+
+def pin_varlen_unpadded(orc):
+    """A padded batch entry equals its own unpadded run; NaN padding is never read."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, Q, K, D, Dv = 3, 4, 2, 5, 14, 16, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    sl = np.array([14, 3, 8], np.int32)
+    kp, vp = k.copy(), v.copy()
+    for b in range(B):
+        kp[b, :, sl[b]:] = np.nan
+        vp[b, :, sl[b]:] = np.nan
+    o, lse = orc.fwd(q, kp, vp, seqlens=sl)
+    o_clean, lse_clean = orc.fwd(q, k, v, seqlens=sl)
+    _close(o, o_clean, 0.0, "NaN padding changes nothing (O)")
+    _close(lse, lse_clean, 0.0, "NaN padding changes nothing (LSE)")
+    for b in range(B):
+        Kb = int(sl[b])
+        ob, lb = orc.fwd(np.ascontiguousarray(q[b:b + 1]), np.ascontiguousarray(k[b:b + 1, :, :Kb]),
+                         np.ascontiguousarray(v[b:b + 1, :, :Kb]))
+        _close(o[b:b + 1], ob, 0.0, f"varlen entry {b} equals its unpadded run (O)")
+        _close(lse[b:b + 1], lb, 0.0, f"varlen entry {b} equals its unpadded run (LSE)")
+
+
+def pin_v_columns_untouched(orc):
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, Q, K, D, Dv = 1, 2, 1, 4, 9, 8, 6
+    q, k = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D))
+    vw = np.full((B, Hkv, K, Dv + 5), np.nan, dtype=np.float32)
+    vw[..., :Dv] = _f32(rng, (B, Hkv, K, Dv))
+    ow = np.full((B, Hq, Q, Dv + 3), 7.25)
+    lse = np.empty((B, Hq, Q))
+    orc.fwd_into(q, k, vw, ow, lse, D=D, Dv=Dv)
+    assert np.all(ow[..., Dv:] == 7.25), "O columns beyond Dv were written"
+    assert np.all(np.isfinite(ow[..., :Dv])), "V columns beyond Dv leaked into O"
+    o_ref, l_ref = orc.fwd(q, k, np.ascontiguousarray(vw[..., :Dv]))
+    _close(ow[..., :Dv], o_ref, 0.0, "wide-row O equals narrow-row O")
+
+
+# ---------------------------------------------------------------- second implementation
+BRUTE_SHAPES = [
+    # B,Hq,Hkv,Q,K,D,Dv, window, seqlens
+    (1, 4, 2, 5, 9, 8, 8, 0, None),
+    (1, 4, 2, 9, 5, 8, 8, 0, None),            # more rows than keys
+    (2, 2, 1, 3, 35, 7, 3, 0, None),           # odd widths
+    (1, 2, 1, 3, 67, 33, 7, 4, None),
+    (3, 4, 4, 4, 12, 16, 8, 3, [0, 12, 5]),
+    (2, 8, 2, 1, 33, 16, 24, 0, [33, 1]),      # decode, MQA-like groups
+]
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(23)
+    for (B, Hq, Hkv, Q, K, D, Dv, W, sl) in BRUTE_SHAPES:
+        q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+        sla = None if sl is None else np.array(sl, np.int32)
+        o, lse = orc.fwd(q, k, v, seqlens=sla, window=W)
+        bo, bl = brute.attention(q, k, v, seqlens=sla, window=W)
+        _close(o, bo, 1e-12, f"brute force O {B,Hq,Hkv,Q,K,D,Dv,W,sl}")
+        _close(lse, bl, 1e-12, f"brute force LSE {B,Hq,Hkv,Q,K,D,Dv,W,sl}")
+
+
+INDEPENDENT_PINS = [
+    pin_worked_examples, pin_textbook_causal, pin_bottom_right, pin_uniform_v, pin_single_key,
+    pin_scale_zero, pin_empty_rows, pin_shift_invariance, pin_probs_sum_to_one, pin_split_merge,
+    pin_gqa_expand, pin_varlen_unpadded, pin_v_columns_untouched,
+]
+ALL_PINS = INDEPENDENT_PINS + [pin_brute_force]

@@ -1,0 +1,54 @@
+"""The fp64 oracle against its pins (CPU only).
+
+The pins live in tests/pins.py; each is a check against something other than
+the oracle itself: hand-worked examples, torch's textbook causal attention,
+closed forms and invariants of the definition.
+"""
+import numpy as np
+import pytest
+
+import pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(orc, pin):
+    pin(orc)
+
+
+def test_oracle_rejects_bad_sizes(orc):
+    from oracle.attn_oracle import OracleError
+    q = np.zeros((1, 3, 2, 4), np.float32)
+    k = np.zeros((1, 2, 5, 4), np.float32)
+    with pytest.raises(OracleError):
+        orc.fwd(q, k, k)  # Hq % Hkv != 0
+    q = np.zeros((1, 2, 2, 4), np.float32)
+    with pytest.raises(OracleError):
+        orc.fwd(q, k, k, seqlens=np.array([6], np.int32))  # length beyond K
+
+
+def test_oracle_rows_match_full(orc):
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 4, 2, 7, 19, 16, 8
+    q = rng.standard_normal((B, Hq, Q, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, K, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, K, Dv)).astype(np.float32)
+    sl = np.array([19, 4], np.int32)
+    o, lse = orc.fwd(q, k, v, seqlens=sl, window=5)
+    rows = np.array([0, 5, 13, 27, 55], np.int64)
+    ro, rl = orc.rows(q, k, v, rows, seqlens=sl, window=5)
+    np.testing.assert_array_equal(ro, o.reshape(-1, Dv)[rows])
+    np.testing.assert_array_equal(rl, lse.reshape(-1)[rows])
+
+
+def test_oracle_bf16_inputs(orc):
+    """bf16 bit patterns are widened exactly: same result as their float32 values."""
+    from attention_attn_fwd_amd import inputs
+    w = inputs.Workload("t", 1, 4, 2, 6, 13, 16, 16)
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    o1, l1 = orc.fwd(q, k, v)
+    f = inputs.bf16_bits_to_f32
+    o2, l2 = orc.fwd(f(q), f(k), f(v))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
