@@ -1,0 +1,146 @@
+"""ctypes binding of libattn_fwd.so (include/attn_fwd.h).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels of the library.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_OOM, ATTN_ERR_HIP = range(5)
+PATH_NONE, PATH_PREFILL, PATH_DECODE = 0, 1, 2
+
+# Every function the header declares; a CPU test checks the library exports all of them.
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_strerror", "attn_fwd_plan")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("split_chunk", ctypes.c_int), ("n_splits", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load():
+    """Load the HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_attn_fwd_amd.build` "
+                              "(there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        sig = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, cf, vp]
+        lib.attn_fwd.argtypes = sig
+        lib.attn_fwd.restype = ci
+        lib.attn_fwd_f32.argtypes = sig
+        lib.attn_fwd_f32.restype = ci
+        lib.attn_fwd_strerror.argtypes = [ci]
+        lib.attn_fwd_strerror.restype = ctypes.c_char_p
+        lib.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Plan)]
+        lib.attn_fwd_plan.restype = ci
+        _lib = lib
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor, or an int / None passed through."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None or isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream on ROCm
+
+
+def strerror(status: int) -> str:
+    return load().attn_fwd_strerror(int(status)).decode()
+
+
+def attn_fwd_strerror(status: int) -> str:
+    return strerror(status)
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream) -> int:
+    """Raw C call (bf16).  Pointers may be tensors or ints; returns the status code."""
+    return load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
+                           _ptr(seqlens_k), int(window), float(scale), _stream(stream))
+
+
+def attn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream) -> int:
+    """Raw C call (fp32).  Pointers may be tensors or ints; returns the status code."""
+    return load().attn_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
+                               _ptr(seqlens_k), int(window), float(scale), _stream(stream))
+
+
+def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
+    plan = _Plan()
+    st = load().attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, int(window), ctypes.byref(plan))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_plan")
+    return {"path": plan.path, "split_chunk": plan.split_chunk, "n_splits": plan.n_splits,
+            "workspace_bytes": plan.workspace_bytes}
+
+
+def forward(q, k, v, seqlens_k=None, window: int = 0, scale: Optional[float] = None, out=None, lse=None,
+            stream=None):
+    """Causal GQA attention forward on torch tensors.
+
+    q [B,Hq,Q,D], k [B,Hkv,K,D], v [B,Hkv,K,Dv]: contiguous, on the GPU, all
+    bfloat16 (bf16 kernels, bf16 output) or all float32 (fp32 kernel).
+    seqlens_k: int32 [B] on the same device, or None.  Returns (o, lse) with
+    o [B,Hq,Q,Dv] in the input dtype and lse [B,Hq,Q] float32.
+    """
+    import torch
+
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must all be bfloat16 or all float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B,H,T,width]")
+    B, Hq, Q, D = q.shape
+    Bk, Hkv, K, Dk = k.shape
+    Bv, Hv, Kv, Dv = v.shape
+    if Bk != B or Bv != B or Hv != Hkv or Kv != K or Dk != D:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if seqlens_k is not None:
+        if seqlens_k.dtype != torch.int32 or seqlens_k.device != q.device or tuple(seqlens_k.shape) != (B,):
+            raise ValueError("seqlens_k must be int32 [B] on the same device")
+        seqlens_k = seqlens_k.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Q, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
+    st = fn(q, k, v, out, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, fn.__name__)
+    return out, lse

@@ -1,0 +1,177 @@
+// C ABI of libattn_fwd.so (declared in include/attn_fwd.h): argument checks,
+// launch planning, stream-ordered scratch for the split-KV path, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "../../include/attn_fwd.h"
+#include "attn_internal.h"
+
+namespace attn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// One private stream-ordered pool per device.  Its release threshold is
+// unbounded, so scratch freed at the end of a call is reused by the next call
+// on the same device instead of going back to the driver at each sync.
+struct DevicePool {
+  std::once_flag once;
+  hipMemPool_t pool = nullptr;
+  hipError_t err = hipSuccess;
+};
+DevicePool g_pools[kMaxDevices];
+
+hipError_t device_pool(int dev, hipMemPool_t* out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  DevicePool& dp = g_pools[dev];
+  std::call_once(dp.once, [&]() {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    dp.err = hipMemPoolCreate(&dp.pool, &props);
+    if (dp.err == hipSuccess) {
+      uint64_t threshold = UINT64_MAX;
+      dp.err = hipMemPoolSetAttribute(dp.pool, hipMemPoolAttrReleaseThreshold, &threshold);
+    }
+  });
+  *out = dp.pool;
+  return dp.err;
+}
+
+bool supported_width(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Keys per split for the decode path: the smallest power of two >= 128 that
+// keeps the grid within about 8 workgroups per CU at full length, capped at
+// 4096 keys.  ATTN_FWD_SPLIT_CHUNK (a multiple of 128) overrides it.
+int split_chunk(int B, int Hkv, int K) {
+  if (const char* e = std::getenv("ATTN_FWD_SPLIT_CHUNK")) {
+    const int v = std::atoi(e);
+    if (v >= kDecodeChunkAlign && v % kDecodeChunkAlign == 0) return v;
+  }
+  const int64_t groups = (int64_t)B * Hkv;
+  const int64_t target = 2048;
+  int ch = kDecodeChunkAlign;
+  while (ch < 4096 && groups * ((K + ch - 1) / ch) > target) ch *= 2;
+  return ch;
+}
+
+// Checks shared by both entry points; fills the plan.
+int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, float scale, bool bf16,
+                   attn_fwd_plan_t* plan) {
+  (void)window;
+  *plan = attn_fwd_plan_t{0, 0, 0, 0};
+  if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * Hq * Q == 0) return ATTN_OK;
+  if (!supported_width(D) || !supported_width(Dv)) return ATTN_ERR_UNSUPPORTED;
+  // Offsets inside one (batch, head) slice are 32-bit in the kernels.
+  const int64_t lim = INT32_MAX;
+  if ((int64_t)Q * D > lim || (int64_t)Q * Dv > lim || (int64_t)K * D > lim || (int64_t)K * Dv > lim)
+    return ATTN_ERR_UNSUPPORTED;
+  const int group = Hq / Hkv;
+  if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows) {
+    plan->path = 2;
+    plan->split_chunk = split_chunk(B, Hkv, K);
+    plan->n_splits = K > 0 ? (K + plan->split_chunk - 1) / plan->split_chunk : 0;
+    const int64_t parts = (int64_t)B * Hkv * plan->n_splits * group * Q;
+    plan->workspace_bytes = parts * (int64_t)(Dv + 2) * 4;
+  } else {
+    plan->path = 1;
+    const int bm = bf16 ? kPrefillBM : kF32Rows;
+    if ((int64_t)((Q + bm - 1) / bm) * Hq * B > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  }
+  return ATTN_OK;
+}
+
+int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
+        int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream_) {
+  attn_fwd_plan_t plan;
+  int st = check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, scale, bf16, &plan);
+  if (st != ATTN_OK || plan.path == 0) return st;
+  if (!q || !o || !lse) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * Hkv * K > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(o) || (k && !aligned16(k)) || (v && !aligned16(v)))
+    return ATTN_ERR_INVALID_ARG;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+  Params p = {};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens_k;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Q = Q; p.K = K; p.D = D; p.Dv = Dv;
+  p.window = window > 0 ? window : 0;
+  p.group = Hq / Hkv;
+  p.q_sign = scale < 0.f ? 1 : 0;
+  p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  p.scale = scale;
+  p.rows = p.group * Q;
+
+  if (!bf16) return launch_fwd_f32(p, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (plan.path == 1) return launch_prefill_bf16(p, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+
+  // Split-KV decode: scratch from the device's stream-ordered pool.
+  p.chunk = plan.split_chunk;
+  p.n_splits = plan.n_splits;
+  const int64_t parts = (int64_t)B * Hkv * plan.n_splits * p.rows;
+  const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
+  if (fail && fail[0] == '1') return ATTN_ERR_OOM;
+  void* ws = nullptr;
+  if (parts > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    hipMemPool_t pool = nullptr;
+    if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipMallocFromPoolAsync(&ws, (size_t)plan.workspace_bytes, pool, stream) != hipSuccess || !ws)
+      return ATTN_ERR_OOM;
+  }
+  float* wsf = static_cast<float*>(ws);
+  p.ws_m = wsf;
+  p.ws_l = wsf + parts;
+  p.ws_acc = wsf + 2 * parts;
+  const hipError_t e = launch_decode_bf16(p, stream);
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (e == hipSuccess && ef != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q, int K,
+             int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream) {
+  return attn::run(true, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int Q,
+                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream) {
+  return attn::run(false, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+}
+
+const char* attn_fwd_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported size (D and Dv must be multiples of 16 in [16, 128])";
+    case ATTN_ERR_OOM: return "scratch allocation failed";
+    case ATTN_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, attn_fwd_plan_t* plan) {
+  if (!plan) return ATTN_ERR_INVALID_ARG;
+  return attn::check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, 1.0f, true, plan);
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Internal declarations of libattn_fwd.so: kernel parameter block, launch
+// helpers and the device-side building blocks shared by the gfx950 kernels.
+// Nothing here is part of the public ABI (include/attn_fwd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Workgroup geometry of the bf16 prefill kernel: 4 waves of 64 lanes, each
+// wave owning 32 query rows (two 16-column MFMA tiles), 64 keys per KV block.
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRowsPerWave = 32;
+constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 128 query rows
+constexpr int kPrefillBN = 64;                                   // keys per block
+
+// Split-KV decode: 4 waves, each consuming 32-key sub-blocks; chunks are
+// multiples of 128 keys so every sub-block lies inside one chunk.
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeSub = 32;
+constexpr int kDecodeChunkAlign = kDecodeWaves * kDecodeSub;
+constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
+constexpr int kDecodeMaxQ = 4;
+
+// fp32 path: one workgroup of 256 threads per (batch, head, 32 query rows).
+constexpr int kF32Rows = 32;
+constexpr int kF32Keys = 32;
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seqlens;  // may be null: every K_b = K
+  int B, Hq, Hkv, Q, K, D, Dv;
+  int window;              // <= 0: none
+  int group;               // Hq / Hkv
+  int q_sign;              // 0x8000 when the scale is negative (q is negated), else 0
+  float scale_log2;        // |scale| * log2(e)
+  float scale;             // raw scale (fp32 path)
+  // split-KV decode scratch
+  float* ws_m;             // [B][Hkv][n_splits][rows]  running max, log2 units
+  float* ws_l;             // [B][Hkv][n_splits][rows]  sum of 2^(s*c - m)
+  float* ws_acc;           // [B][Hkv][n_splits][rows][Dv] unnormalised P.V
+  int chunk;               // keys per split (multiple of kDecodeChunkAlign)
+  int n_splits;            // ceil(K / chunk)
+  int rows;                // group * Q
+};
+
+// Launchers (each returns hipGetLastError() after the launch).
+hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream);
+hipError_t launch_decode_bf16(const Params& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
+
+// Padded widths the kernels are instantiated for.
+inline int pad_width(int d) { return d <= 64 ? 64 : 128; }
+
+// ---------------------------------------------------------------------------
+// Device building blocks
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int K) {
+  if (!seqlens) return K;
+  int s = seqlens[b];
+  return s < 0 ? 0 : (s > K ? K : s);
+}
+
+// v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]
+// (e = 0..7) and receives C[4(l/16)+r][l%16] (r = 0..3).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, output
+// lane c element r is element c%4 of the 8 bytes addressed by lane 4r + c/4.
+// With lane i of the group addressing row (base + i/4), columns 4(i%4)..+3 of
+// a row-major 16-bit tile, lane c receives column c of rows base..base+3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Butterfly over lanes l, l^16, l^32, l^48 using the gfx950 permlane swaps.
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack eight floats into bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+__device__ __forceinline__ uint4 load_u4(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace attn

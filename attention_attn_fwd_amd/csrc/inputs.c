@@ -61,31 +61,48 @@ void attn_inputs_f32_to_bf16(const float* in, uint16_t* out, int64_t n) {
 static const double TWO_PI = 6.283185307179586476925286766559;
 static const double INV_2_32 = 1.0 / 4294967296.0;
 
-/* Normal sample for global element index i of stream (seed, tensor_id). */
-static double normal_at(uint64_t i, uint32_t seed, uint32_t tensor_id) {
-  uint64_t blk = i >> 2;
+/* The four normals of Philox block `blk` of stream (seed, tensor_id). */
+static void normals_of_block(uint64_t blk, uint32_t seed, uint32_t tensor_id, double z[4]) {
   uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u};
   uint32_t key[2] = {seed, tensor_id};
   uint32_t w[4];
   philox4x32_10(ctr, key, w);
-  int lane = (int)(i & 3);
-  int pair = lane >> 1;
-  double u1 = ((double)w[2 * pair] + 0.5) * INV_2_32;     /* in (0,1) */
-  double u2 = ((double)w[2 * pair + 1] + 0.5) * INV_2_32; /* in (0,1) */
-  double r = sqrt(-2.0 * log(u1));
-  double t = TWO_PI * u2;
-  return (lane & 1) ? r * sin(t) : r * cos(t);
+  for (int pair = 0; pair < 2; ++pair) {
+    double u1 = ((double)w[2 * pair] + 0.5) * INV_2_32;     /* in (0,1) */
+    double u2 = ((double)w[2 * pair + 1] + 0.5) * INV_2_32; /* in (0,1) */
+    double r = sqrt(-2.0 * log(u1));
+    double t = TWO_PI * u2;
+    z[2 * pair] = r * cos(t);
+    z[2 * pair + 1] = r * sin(t);
+  }
 }
 
-/* out[j] = bf16(normal(offset + j)) for j < n.  threads <= 0: runtime default. */
+/* Calls emit(j, z) for every element j in [0, n) of the slice starting at
+ * global index `offset`, visiting each Philox block once. */
+#define FOR_EACH_NORMAL(n, offset, seed, tensor_id, threads, EMIT)                                   \
+  do {                                                                                             \
+    const uint64_t first = (uint64_t)(offset), last = (uint64_t)(offset) + (uint64_t)(n);          \
+    const int64_t b0 = (int64_t)(first >> 2), b1 = (int64_t)((last + 3) >> 2);                     \
+    _Pragma("omp parallel for schedule(static) num_threads(threads > 0 ? threads : omp_get_max_threads())") \
+    for (int64_t blk = b0; blk < b1; ++blk) {                                                      \
+      double z[4];                                                                                 \
+      normals_of_block((uint64_t)blk, seed, tensor_id, z);                                         \
+      for (int e = 0; e < 4; ++e) {                                                                \
+        uint64_t i = ((uint64_t)blk << 2) + (uint64_t)e;                                           \
+        if (i < first || i >= last) continue;                                                      \
+        int64_t j = (int64_t)(i - first);                                                          \
+        EMIT;                                                                                      \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+
+/* out[j] = bf16(float(normal(offset + j))) for j < n.  threads <= 0: runtime default. */
 void attn_inputs_normal_bf16(uint16_t* out, int64_t n, int64_t offset, uint32_t seed, uint32_t tensor_id, int threads) {
-#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : omp_get_max_threads())
-  for (int64_t j = 0; j < n; ++j) out[j] = f32_to_bf16_rne((float)normal_at((uint64_t)(offset + j), seed, tensor_id));
+  FOR_EACH_NORMAL(n, offset, seed, tensor_id, threads, out[j] = f32_to_bf16_rne((float)z[e]));
 }
 
 void attn_inputs_normal_f32(float* out, int64_t n, int64_t offset, uint32_t seed, uint32_t tensor_id, int threads) {
-#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : omp_get_max_threads())
-  for (int64_t j = 0; j < n; ++j) out[j] = (float)normal_at((uint64_t)(offset + j), seed, tensor_id);
+  FOR_EACH_NORMAL(n, offset, seed, tensor_id, threads, out[j] = (float)z[e]);
 }
 
 /* Uniform 32-bit words: out[j] = word (offset+j)%4 of block (offset+j)/4. */

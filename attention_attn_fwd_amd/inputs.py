@@ -190,11 +190,30 @@ class Workload:
     def gen_q(self, threads: int = 0):
         return normal(self.q_shape(), TID_Q, self.seed, self.dtype, threads=threads)
 
-    def gen_k(self, threads: int = 0):
-        return normal(self.k_shape(), TID_K, self.seed, self.dtype, threads=threads)
+    def gen_k(self, threads: int = 0, padding: str = "normal"):
+        return self._gen_kv(self.k_shape(), TID_K, threads, padding)
 
-    def gen_v(self, threads: int = 0):
-        return normal(self.v_shape(), TID_V, self.seed, self.dtype, threads=threads)
+    def gen_v(self, threads: int = 0, padding: str = "normal"):
+        return self._gen_kv(self.v_shape(), TID_V, threads, padding)
+
+    def _gen_kv(self, shape, tid, threads, padding):
+        """K or V.  padding="normal" fills every row from the stream; "zero" fills
+        only rows k < K_b (same values as "normal" there) and leaves the padding
+        rows zero, which the attention never reads, to save generation time on
+        long padded caches."""
+        if padding == "normal" or self.seqlens is None:
+            return normal(shape, tid, self.seed, self.dtype, threads=threads)
+        if padding != "zero":
+            raise ValueError(f"padding must be 'normal' or 'zero', got {padding!r}")
+        arr = np.zeros(shape, dtype=np.uint16 if self.dtype == "bf16" else np.float32)
+        B, H, T, W = shape
+        for b in range(B):
+            kb = self.kb(b)
+            for hh in range(H):
+                if kb > 0:
+                    normal((kb, W), tid, self.seed, self.dtype, offset=((b * H + hh) * T) * W,
+                           threads=threads, out=arr[b, hh, :kb])
+        return arr
 
     def gen_rows(self, which: str, b: int, head: int, r0: int, r1: int) -> np.ndarray:
         """Regenerate rows [r0, r1) of one (batch, head) slice of Q, K or V on its own."""

@@ -1,0 +1,256 @@
+"""Benchmark of the causal GQA attention forward on one MI355X.
+
+One step is one pass of the whole hot path over resident inputs: one
+attn_fwd call on the dense causal GQA prefill (B=4, Hq=32, Hkv=8, Q=K=4096,
+D=Dv=128: the bf16 MFMA prefill kernel) and one attn_fwd call on the batched
+long-context decode (B=64, Hq=64, Hkv=8, Q=1, int32 KV lengths log-uniform in
+[1024, 32768] padded to 32768, D=Dv=128: split-KV decode + log-sum-exp
+combine).  Inputs are seeded N(0,1) rounded to bf16 (Philox, seed 1234).
+
+Reported: prefill TFLOP/s (2*(D+Dv) per legal (row, key) pair) and decode KV
+GB/s (K_b*Hkv*(D+Dv)*2 bytes summed over sequences), each against its
+roofline (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  `value` is the whole
+step's fraction of roofline: the time the step would take at both peaks
+divided by the measured step time, in percent.
+
+The fp64 oracle is timed on a bounded sample of rows of the same two
+workloads on the host cores as a reported CPU baseline (never the target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "causal GQA attn fwd: prefill TFLOP/s + decode KV GB/s, % of roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["attn_internal.h", "prefill_bf16.hip", "decode_bf16.hip"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_attn_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("kernel_digest") != digest:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Problem:
+    def __init__(self, w, torch):
+        from attention_attn_fwd_amd import inputs  # noqa: F401
+        t0 = time.time()
+        self.w = w
+        q = w.gen_q()
+        k = w.gen_k(padding="zero")
+        v = w.gen_v(padding="zero")
+        dev = "cuda:0"
+        self.q = torch.from_numpy(q).to(dev).view(torch.bfloat16)
+        self.k = torch.from_numpy(k).to(dev).view(torch.bfloat16)
+        self.v = torch.from_numpy(v).to(dev).view(torch.bfloat16)
+        self.host = (q, k, v)  # kept for the CPU baseline
+        self.seq = None if w.seqlens is None else torch.from_numpy(np.asarray(w.seqlens, np.int32)).to(dev)
+        self.o = torch.empty(w.o_shape(), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.B, w.Hq, w.Q), dtype=torch.float32, device=dev)
+        self.pairs = w.legal_pairs()
+        self.flops = 2.0 * (w.D + w.Dv) * self.pairs
+        self.kv_bytes = float(w.kv_tokens()) * (w.D + w.Dv) * 2
+        log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s "
+            f"(pairs {self.pairs}, flops {self.flops:.4e}, kv bytes {self.kv_bytes:.4e})")
+
+    def call(self, af, stream):
+        w = self.w
+        st = af.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv,
+                         self.seq, w.window, w.scale, stream)
+        if st != af.ATTN_OK:
+            raise RuntimeError(f"attn_fwd failed on {w.name}: {af.strerror(st)}")
+
+
+def cpu_baseline(probs, budget_s: float):
+    """Time the fp64 oracle on bounded samples of rows of the step's workloads."""
+    from oracle import attn_oracle
+    orc = attn_oracle.load()
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+    for tag, pr in probs:
+        w = pr.w
+        rng = np.random.default_rng(7)
+        q, k, v = pr.host
+        kb = np.array([w.kb(b) for b in range(w.B)])
+        done_rows, done_flops, elapsed = 0, 0.0, 0.0
+        batch = 256 if tag == "prefill" else 64
+        while elapsed < budget_s / len(probs):
+            rows = rng.integers(0, w.B * w.Hq * w.Q, size=batch).astype(np.int64)
+            b = rows // (w.Hq * w.Q)
+            qi = rows % w.Q
+            p = qi + kb[b] - w.Q
+            hi = np.minimum(kb[b] - 1, p)
+            lo = np.zeros_like(hi) if w.window <= 0 else np.maximum(0, p - w.window + 1)
+            pairs = np.maximum(hi - lo + 1, 0).sum()
+            t0 = time.perf_counter()
+            orc.rows(q, k, v, rows, seqlens=w.seqlens, window=w.window, scale=w.scale, threads=threads)
+            elapsed += time.perf_counter() - t0
+            done_rows += len(rows)
+            done_flops += 2.0 * (w.D + w.Dv) * float(pairs)
+        out[tag] = {"rows": done_rows, "seconds": elapsed, "flops": done_flops}
+    return out, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["step", "prefill", "decode"], default="step",
+                    help="time the whole step (default) or one of its two calls alone (for profiling)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this attention forward has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_attn_fwd_amd as af
+    from attention_attn_fwd_amd import inputs
+
+    af.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    prefill_w, decode_w = inputs.config(3), inputs.config(5)
+    probs = []
+    if args.workload in ("step", "prefill"):
+        probs.append(("prefill", Problem(prefill_w, torch)))
+    if args.workload in ("step", "decode"):
+        probs.append(("decode", Problem(decode_w, torch)))
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        for _, pr in probs:
+            pr.call(af, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # Events on the stream every kernel is launched on: one before each call and one after the last.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(probs) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, pr) in enumerate(probs):
+            ev[s][i].record(stream)
+            pr.call(af, stream)
+        ev[s][len(probs)].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per_call = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) * 1e-3 for s in range(args.steps)]
+                for i, (name, _) in enumerate(probs)}
+    step_times = [ev[s][0].elapsed_time(ev[s][len(probs)]) * 1e-3 for s in range(args.steps)]
+    ms_per_step = 1e3 * float(np.mean(step_times))
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f} ms/step)")
+
+    digest = kernel_digest()
+    parts, ideal, measured = {}, 0.0, 0.0
+    for name, pr in probs:
+        t = float(np.mean(per_call[name]))
+        measured += t
+        if name == "prefill":
+            achieved = pr.flops / t / 1e12
+            peak, unit, bound = PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+            ideal += pr.flops / (PEAK_BF16_TFLOPS * 1e12)
+            traffic = measured_traffic("prefill_bf16_kernel", digest)
+        else:
+            achieved = pr.kv_bytes / t / 1e9
+            peak, unit, bound = PEAK_HBM_GBS, "GB/s", "hbm"
+            ideal += pr.kv_bytes / (PEAK_HBM_GBS * 1e9)
+            traffic = measured_traffic("decode_split_kernel", digest)
+        parts[name] = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                       "frac": achieved / peak, "traffic": traffic, "us_per_call": 1e6 * t,
+                       "us_min": 1e6 * float(np.min(per_call[name])), "workload": pr.w.name}
+        log(f"[bench] {name}: {1e6 * t:.1f} us/call, {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of peak")
+    frac = ideal / measured
+    dominant = max(parts, key=lambda n: parts[n]["us_per_call"])
+    roof = {k: parts[dominant][k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        samples, threads = cpu_baseline(probs, args.cpu_budget)
+        # Extrapolate the oracle's rate on each workload to the whole step.
+        t_cpu = 0.0
+        desc = []
+        for name, pr in probs:
+            smp = samples[name]
+            rate = smp["flops"] / smp["seconds"]
+            t_cpu += pr.flops / rate
+            desc.append(f"{smp['rows']} random rows of the {name} workload ({smp['seconds']:.1f}s, "
+                        f"{rate / 1e9:.2f} GFLOP/s fp64)")
+        cpu = {"value": 100.0 * ideal / t_cpu, "unit": "% of roofline", "cores": threads, "kind": "oracle",
+               "sample": "; ".join(desc) + "; step time extrapolated by algorithmic flops",
+               "seconds_per_step": t_cpu}
+        log(f"[bench] cpu baseline: {t_cpu:.1f} s/step extrapolated on {threads} threads")
+
+    w3, w5 = prefill_w, decode_w
+    workload = []
+    if "prefill" in parts:
+        workload.append(f"dense causal GQA prefill B={w3.B},Hq={w3.Hq},Hkv={w3.Hkv},Q=K={w3.K},D=Dv={w3.D}")
+    if "decode" in parts:
+        workload.append(f"batched long-context decode B={w5.B},Hq={w5.Hq},Hkv={w5.Hkv},Q=1,"
+                        f"K_b log-uniform [1024,32768] padded to {w5.K},D=Dv={w5.D}")
+    rec = {
+        "metric": METRIC,
+        "value": 100.0 * frac,
+        "unit": "% of roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16 (Philox-4x32-10, seed 1234)",
+        "config": {"workload": " + ".join(workload), "seed": 1234, "parallelism": "single GPU"},
+        "prefill_tflops": parts.get("prefill", {}).get("achieved"),
+        "decode_kv_gbs": parts.get("decode", {}).get("achieved"),
+        "roofline": roof,
+        "roofline_by_call": parts,
+        "kernel_digest": digest,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

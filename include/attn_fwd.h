@@ -1,0 +1,105 @@
+/*
+ * attn_fwd.h - C ABI of libattn_fwd.so: causal grouped-query attention
+ * forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the attention fixture of the LuisaCompute "Attention
+ * execution mapping" review, section 1: bottom-right causal GQA in which
+ * query head h reads kv-head h / (Hq/Hkv) and key k is legal for query row q
+ * when k <= q + K - Q, with the online-softmax state (row max, row sum,
+ * accumulator) carried across KV blocks so one program covers prefill and
+ * decode.  Int32 per-sequence lengths, unequal lengths, empty sequences,
+ * sliding windows and finite padded rows come from the attention feature
+ * list of the Laya "Fast backends" page (sections "TileLang portability" and
+ * "Numerics").  Readings taken where the pages are silent:
+ *   - with lengths, K_b = seqlens_k[b] replaces K in the offset:
+ *     p(q) = q + K_b - Q, and keys k >= K_b do not exist;
+ *   - window W > 0 keeps the W keys p(q)-W < k <= p(q); W <= 0 disables it;
+ *   - a row with no legal key gets O = 0 and LSE = -inf;
+ *   - LSE = ln(sum over legal k of exp(scale * q.k)), stored as float.
+ *
+ * Layouts: contiguous row-major [B, H, T, width] for every tensor:
+ *   q [B, Hq, Q, D], k [B, Hkv, K, D], v [B, Hkv, K, Dv],
+ *   o [B, Hq, Q, Dv], lse [B, Hq, Q] (float).
+ * K is the padded key length; seqlens_k (int32[B], device memory) may be
+ * NULL, meaning every K_b = K.  Base pointers must be 16-byte aligned.
+ *
+ * Every pointer argument is a DEVICE pointer.  `stream` is a hipStream_t
+ * passed as void* (NULL = the null stream).  Calls are asynchronous: they
+ * return after enqueueing kernels on `stream`, with no host synchronisation;
+ * a device fault surfaces at the caller's next synchronisation.
+ *
+ * Ownership: the caller owns every buffer.  The library keeps no pointer past
+ * the call's stream-ordered completion and frees nothing it did not
+ * allocate.  Inputs are only read.  o and lse must not alias the inputs.
+ * Scratch for the split-KV decode path comes from a library-owned,
+ * stream-ordered HIP memory pool (allocated and released on `stream`), so
+ * concurrent calls on different streams do not share scratch.
+ *
+ * seqlens_k is never read on the host.  Values outside [0, K] are a caller
+ * error; the kernels clamp them to [0, K] so memory outside the tensors is
+ * never touched.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* nothing launched */
+  ATTN_ERR_UNSUPPORTED = 2, /* nothing launched */
+  ATTN_ERR_OOM = 3,         /* scratch allocation failed; nothing launched */
+  ATTN_ERR_HIP = 4          /* a HIP call or launch failed */
+};
+
+/*
+ * bf16 inputs (q, k, v as bfloat16), bf16 output o, float lse.
+ * Scores, softmax state and accumulators are float; the weights P are
+ * rounded to bf16 before the P.V product (GPU intermediates keep the input
+ * type, Laya "Fast backends", "TileLang portability").
+ *
+ * Returns:
+ *   ATTN_ERR_INVALID_ARG  a negative size; Hq > 0 with Hkv == 0 or
+ *                         Hq % Hkv != 0; a non-finite scale; q/o/lse NULL
+ *                         while B*Hq*Q > 0; k/v NULL while B*Hkv*K > 0;
+ *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 128];
+ *   ATTN_ERR_OOM, ATTN_ERR_HIP as above;
+ *   ATTN_OK               also when B*Hq*Q == 0 (nothing launched).
+ * K == 0, or every K_b == 0, writes O = 0 and LSE = -inf for all rows.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q, int K,
+             int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream);
+
+/* Same contract with float q, k, v and float o; all arithmetic in float. */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int Q,
+                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* attn_fwd_strerror(int status);
+
+/*
+ * The launch plan attn_fwd would use for these sizes, without launching
+ * anything (host only).  path: 0 = no launch, 1 = prefill kernel,
+ * 2 = split-KV decode + combine.  split_chunk is the keys per split (decode
+ * path, else 0) and n_splits the splits per (batch, kv-head) at length K;
+ * workspace_bytes the scratch the decode path takes from the pool.
+ * Returns the status attn_fwd would return for an argument check.
+ */
+typedef struct attn_fwd_plan_t {
+  int path;
+  int split_chunk;
+  int n_splits;
+  int64_t workspace_bytes;
+} attn_fwd_plan_t;
+
+int attn_fwd_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, attn_fwd_plan_t* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,88 @@
+"""The C-ABI library on the CPU: it loads, exports every declared function, and
+rejects bad arguments before touching the GPU (no kernel is launched here)."""
+import os
+import re
+
+import pytest
+
+import attention_attn_fwd_amd as af
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    lib = af.load()
+    declared = _declared_functions()
+    assert set(af.EXPORTS) == set(declared), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror():
+    for st in range(5):
+        assert af.strerror(st)
+    assert af.strerror(99) == "unknown status"
+
+
+BAD = [
+    # B, Hq, Hkv, Q, K, D, Dv, scale, expected
+    (-1, 4, 2, 8, 8, 64, 64, 1.0, af.ATTN_ERR_INVALID_ARG),
+    (1, 4, 3, 8, 8, 64, 64, 1.0, af.ATTN_ERR_INVALID_ARG),     # Hq % Hkv
+    (1, 4, 0, 8, 8, 64, 64, 1.0, af.ATTN_ERR_INVALID_ARG),     # Hkv = 0 < Hq
+    (1, 4, 2, 8, 8, 64, 64, float("nan"), af.ATTN_ERR_INVALID_ARG),
+    (1, 4, 2, 8, 8, 64, 64, float("inf"), af.ATTN_ERR_INVALID_ARG),
+    (1, 4, 2, 8, 8, 72, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),     # D % 16
+    (1, 4, 2, 8, 8, 64, 7, 1.0, af.ATTN_ERR_UNSUPPORTED),
+    (1, 4, 2, 8, 8, 256, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 128
+    (1, 4, 2, 8, 8, 0, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("case", BAD)
+@pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
+def test_bad_arguments_rejected_before_launch(fn, case):
+    B, Hq, Hkv, Q, K, D, Dv, scale, want = case
+    fake = 1 << 20  # never dereferenced: the checks come first
+    assert fn(fake, fake, fake, fake, fake, B, Hq, Hkv, Q, K, D, Dv, None, 0, scale, None) == want
+
+
+@pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
+def test_null_and_misaligned_pointers(fn):
+    fake = 1 << 20
+    assert fn(None, fake, fake, fake, fake, 1, 4, 2, 8, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_ERR_INVALID_ARG
+    assert fn(fake, None, fake, fake, fake, 1, 4, 2, 8, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_ERR_INVALID_ARG
+    assert fn(fake, fake, fake, fake, None, 1, 4, 2, 8, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_ERR_INVALID_ARG
+    assert fn(fake + 2, fake, fake, fake, fake, 1, 4, 2, 8, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
+def test_empty_problem_is_ok_without_launch(fn):
+    for (B, Hq, Q) in [(0, 4, 8), (1, 0, 8), (2, 4, 0)]:
+        Hkv = 2 if Hq else 0
+        assert fn(None, None, None, None, None, B, Hq, Hkv, Q, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_OK
+
+
+def test_plan_selects_paths():
+    assert af.attn_fwd_plan(4, 32, 8, 4096, 4096, 128, 128)["path"] == af.PATH_PREFILL
+    p = af.attn_fwd_plan(64, 64, 8, 1, 32768, 128, 128)
+    assert p["path"] == af.PATH_DECODE and p["split_chunk"] % 128 == 0
+    assert p["n_splits"] == -(-32768 // p["split_chunk"])
+    assert p["workspace_bytes"] == 64 * 8 * p["n_splits"] * 8 * (128 + 2) * 4
+    assert af.attn_fwd_plan(1, 8, 2, 1, 2053, 80, 96)["path"] == af.PATH_DECODE
+    assert af.attn_fwd_plan(1, 8, 2, 4, 100, 64, 64)["path"] == af.PATH_DECODE      # 16 packed rows
+    assert af.attn_fwd_plan(1, 64, 1, 1, 100, 64, 64)["path"] == af.PATH_PREFILL    # 64 rows: prefill kernel
+    assert af.attn_fwd_plan(1, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_PREFILL
+    assert af.attn_fwd_plan(0, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_NONE
+    assert af.attn_fwd_plan(1, 8, 2, 1, 0, 64, 64)["n_splits"] == 0
+    with pytest.raises(af.AttnError):
+        af.attn_fwd_plan(1, 8, 3, 1, 10, 64, 64)

@@ -1,0 +1,75 @@
+"""The five benchmark workloads at full size, in the launch configuration the
+bench times.  The two small ones are compared against the oracle in full; the
+three large ones on sampled rows (the oracle computes rows one by one), plus
+whole-output properties that hold at any size: every row written, no NaN/Inf,
+LSE = -inf exactly on the rows without a legal key, bitwise-identical reruns.
+"""
+import numpy as np
+import pytest
+
+from attention_attn_fwd_amd import inputs
+from gpu_util import compare, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_rows(w, n, seed=0):
+    """Flat row ids (b*Hq+h)*Q+q: tile edges, first/last rows, and random rows."""
+    rng = np.random.default_rng(seed)
+    qs = {0, w.Q - 1}
+    for edge in (127, 128, 255, 256, w.Q // 2):
+        if 0 <= edge < w.Q:
+            qs.add(edge)
+    rows = set()
+    for b in range(w.B):
+        for q in qs:
+            rows.add((b * w.Hq + int(rng.integers(w.Hq))) * w.Q + q)
+    while len(rows) < n:
+        rows.add(int(rng.integers(w.B * w.Hq * w.Q)))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _empty_rows_mask(w):
+    """True where a row has no legal key: q + K_b - Q < 0 (the window always keeps the diagonal)."""
+    kb = np.array([w.kb(b) for b in range(w.B)])[:, None, None]
+    q = np.arange(w.Q)[None, None, :]
+    return np.broadcast_to(q + kb - w.Q < 0, (w.B, w.Hq, w.Q))
+
+
+def _run_config(idx, orc, n_rows):
+    w = inputs.config(idx)
+    say(f"[config {idx}] {w.name} {w.shape_tuple} {w.dtype} W={w.window}")
+    q = w.gen_q()
+    k = w.gen_k(padding="zero")
+    v = w.gen_v(padding="zero")
+    o, lse = run_gpu(w, q, k, v, check_inputs=(idx <= 3))
+    empty = _empty_rows_mask(w)
+    assert np.array_equal(np.isneginf(lse), empty), "LSE -inf pattern differs from the rows without keys"
+    assert np.all(o[empty] == 0.0)
+    assert np.isfinite(o).all() and not np.isnan(lse).any()
+    if n_rows is None:
+        ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
+        return compare(o, lse, ro, rl, w.dtype, w.name)
+    rows = _sample_rows(w, n_rows)
+    ro, rl = orc.rows(q, k, v, rows, seqlens=w.seqlens, window=w.window, scale=w.scale)
+    return compare(o.reshape(-1, w.Dv)[rows], lse.reshape(-1)[rows], ro, rl, w.dtype, f"{w.name} ({len(rows)} rows)")
+
+
+def test_config1_tiny_fp32(orc):
+    _run_config(1, orc, None)
+
+
+def test_config2_decode_tail(orc):
+    _run_config(2, orc, None)
+
+
+def test_config3_dense_prefill(orc):
+    _run_config(3, orc, 384)
+
+
+def test_config4_varlen_window(orc):
+    _run_config(4, orc, 384)
+
+
+def test_config5_long_decode(orc):
+    _run_config(5, orc, 768)

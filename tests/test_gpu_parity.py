@@ -1,0 +1,194 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Inputs are seeded (Philox, seed 1234 unless stated) and rounded to bf16 before
+either side sees them.  Every call writes into NaN-prefilled outputs followed
+by canary bands; inputs are checksummed before and after; a second call must
+be bitwise identical.  Tolerances are max abs over all elements: 2e-2 on O
+and 1e-3 on LSE for bf16, 1e-4 for the fp32 path; -inf LSE must match exactly.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import attention_attn_fwd_amd as af
+from attention_attn_fwd_amd import inputs
+from gpu_util import Outputs, call, compare, run_gpu, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, scale=None, window=None, orc=None, tag=""):
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    say(f"[case] {w.name} {w.shape_tuple} {w.dtype} W={w.window if window is None else window} "
+        f"seqlens={None if w.seqlens is None else list(w.seqlens)} scale={w.scale if scale is None else scale} {tag}")
+    o, lse = run_gpu(w, q, k, v, scale=scale, window=window)
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window if window is None else window,
+                     scale=w.scale if scale is None else scale)
+    return compare(o, lse, ro, rl, w.dtype, w.name + tag)
+
+
+# Validation matrix: prefill held-out shapes with Q/K tails, the decode anchors,
+# small-Q, MQA/MHA groups, long KV, and D != Dv.
+SHAPES = [
+    (1, 4, 2, 64, 128, 64, 64),
+    (1, 4, 2, 65, 131, 64, 64),
+    (1, 8, 2, 256, 1024, 64, 64),
+    (1, 8, 2, 1, 2048, 64, 64),
+    (1, 8, 2, 1, 2053, 80, 96),
+    (1, 16, 4, 1, 4096, 128, 128),
+    (1, 8, 2, 3, 67, 80, 96),
+    (1, 4, 2, 65, 65, 64, 64),
+    (2, 8, 1, 1, 2053, 80, 96),
+    (1, 8, 8, 1, 2048, 64, 64),
+    (1, 16, 4, 1, 8193, 128, 128),
+    (1, 8, 2, 1, 32768, 64, 96),
+    (2, 8, 2, 300, 300, 128, 128),
+    (1, 4, 1, 200, 700, 128, 64),
+    (1, 4, 2, 130, 90, 64, 128),     # more rows than keys
+    (1, 16, 2, 4, 500, 128, 128),    # 32 packed decode rows
+    (1, 64, 1, 1, 300, 64, 64),      # 64 packed rows: prefill kernel at Q = 1
+    (3, 6, 3, 2, 777, 16, 32),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shape_matrix(orc, shape, dtype):
+    w = inputs.Workload("shape", *shape, dtype=dtype)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("window", [1, 2, 63, 64, 65, 130, 1023, 1024, 5000])
+def test_sliding_window_prefill(orc, window, dtype):
+    w = inputs.Workload("window_prefill", 1, 4, 2, 200, 333, 64, 64, dtype=dtype, window=window)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("window", [1, 5, 100, 2053])
+@pytest.mark.parametrize("Q", [1, 3])
+def test_sliding_window_decode(orc, window, Q):
+    w = inputs.Workload("window_decode", 2, 8, 2, Q, 2053, 80, 96, window=window)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Q", [1, 2, 4, 160])
+def test_varlen(orc, Q, dtype):
+    sl = np.array([0, 1, 7, 64, 129, 160, 33, 0], np.int32)
+    w = inputs.Workload("varlen", 8, 8, 2, Q, 160, 64, 64, dtype=dtype, seqlens=sl)
+    _check(w, orc=orc)
+    _check(w, window=20, orc=orc, tag=" W=20")
+
+
+@pytest.mark.parametrize("K", [0, 1, 7, 16, 31, 32, 33, 63, 64, 65, 127, 128, 129])
+@pytest.mark.parametrize("Q", [1, 4, "K"])
+def test_short_lengths(orc, K, Q):
+    q_len = K if Q == "K" else Q
+    if q_len == 0:
+        q_len = 1
+    w = inputs.Workload("short", 2, 4, 2, q_len, K, 128, 128)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("Q", [1, 77])
+def test_scales(orc, scale, Q, dtype):
+    w = inputs.Workload("scale", 1, 4, 2, Q, 190, 64, 64, dtype=dtype)
+    _check(w, scale=scale, orc=orc)
+
+
+@pytest.mark.parametrize("Q", [1, 3, 100])
+def test_nan_padding_is_never_read(orc, Q):
+    """K/V rows at k >= K_b set to NaN change nothing (bitwise)."""
+    import torch
+    sl = np.array([100, 37, 0, 64], np.int32)
+    w = inputs.Workload("poison", 4, 4, 2, Q, 128, 64, 64, seqlens=sl)
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    o1, l1 = run_gpu(w, q, k, v, check_inputs=False, repeat_bitwise=False)
+    kp, vp = k.copy(), v.copy()
+    for b in range(w.B):
+        kp[b, :, sl[b]:] = 0x7FC0
+        vp[b, :, sl[b]:] = 0x7FC0
+    o2, l2 = run_gpu(w, q, kp, vp, check_inputs=False, repeat_bitwise=False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    ro, rl = orc.fwd(q, k, v, seqlens=sl)
+    compare(o2, l2, ro, rl, "bf16", "poisoned padding")
+
+
+def test_empty_sequences_write_zero_and_neg_inf(orc):
+    w = inputs.Workload("all_empty", 3, 4, 2, 5, 64, 64, 64, seqlens=np.zeros(3, np.int32))
+    o, lse = run_gpu(w, w.gen_q(), w.gen_k(), w.gen_v())
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+    w = inputs.Workload("all_empty_decode", 3, 4, 2, 1, 64, 64, 64, seqlens=np.zeros(3, np.int32))
+    o, lse = run_gpu(w, w.gen_q(), w.gen_k(), w.gen_v())
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_zero_work_is_a_noop():
+    import torch
+    w = inputs.Workload("noop", 2, 4, 2, 0, 16, 64, 64)
+    outs = Outputs(inputs.Workload("buf", 2, 4, 2, 1, 16, 64, 64), "bf16")
+    before = outs.o_raw.clone()
+    d = to_dev(np.zeros(16, np.uint16))
+    st = af.attn_fwd(d, d, d, outs.o, outs.l, 2, 4, 2, 0, 16, 64, 64, None, 0, 1.0,
+                     torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert st == af.ATTN_OK and torch.equal(before, outs.o_raw)
+
+
+def test_forced_scratch_failure_reports_oom():
+    import torch
+    w = inputs.Workload("oom", 1, 8, 2, 1, 300, 64, 64)
+    dq, dk, dv = to_dev(w.gen_q()), to_dev(w.gen_k()), to_dev(w.gen_v())
+    outs = Outputs(w, "bf16")
+    os.environ["ATTN_FWD_FAIL_ALLOC"] = "1"
+    try:
+        st = call(w, dq, dk, dv, None, outs)
+    finally:
+        del os.environ["ATTN_FWD_FAIL_ALLOC"]
+    assert st == af.ATTN_ERR_OOM
+    torch.cuda.synchronize()
+    assert torch.isnan(outs.o.float()).all()
+
+
+def test_invalid_arguments_on_device():
+    import torch
+    w = inputs.Workload("bad", 1, 4, 2, 8, 16, 64, 64)
+    d = to_dev(w.gen_q())
+    s = torch.cuda.current_stream()
+    assert af.attn_fwd(d, d, d, d, d, 1, 4, 3, 8, 16, 64, 64, None, 0, 1.0, s) == af.ATTN_ERR_INVALID_ARG
+    assert af.attn_fwd(d, d, d, d, d, 1, 4, 2, 8, 16, 48 + 8, 64, None, 0, 1.0, s) == af.ATTN_ERR_UNSUPPORTED
+
+
+def test_forward_api_matches_raw_call(orc):
+    import torch
+    w = inputs.Workload("forward", 2, 8, 2, 33, 150, 64, 64, seqlens=np.array([150, 90], np.int32))
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    o, lse = af.forward(to_dev(q), to_dev(k), to_dev(v), seqlens_k=to_dev(w.seqlens))
+    torch.cuda.synchronize()
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens)
+    compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16",
+            "forward()")
+
+
+def test_streams_are_honoured(orc):
+    """A call on a side stream, waited on by the default stream, gives the same result."""
+    import torch
+    w = inputs.Workload("stream", 1, 8, 2, 1, 5000, 128, 128)
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    side = torch.cuda.Stream()
+    outs = Outputs(w, "bf16")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st = call(w, dq, dk, dv, None, outs, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert st == af.ATTN_OK
+    o, lse = outs.host()
+    ro, rl = orc.fwd(q, k, v)
+    compare(o, lse, ro, rl, "bf16", "side stream")

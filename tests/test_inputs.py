@@ -112,3 +112,13 @@ def test_seqlens_uniform_covers_range():
     s = inputs.seqlens_uniform(20000, 4096, seed=7)
     assert s.min() >= 0 and s.max() <= 4096
     assert abs(s.mean() - 2048) < 40
+
+
+def test_zero_padding_keeps_valid_rows():
+    w = inputs.Workload("t", 3, 4, 2, 2, 37, 16, 32, seqlens=np.array([37, 0, 11], np.int32))
+    full, lean = w.gen_k(), w.gen_k(padding="zero")
+    for b in range(3):
+        kb = w.kb(b)
+        np.testing.assert_array_equal(lean[b, :, :kb], full[b, :, :kb])
+        assert not lean[b, :, kb:].any()
+    np.testing.assert_array_equal(w.gen_v(padding="zero")[2, :, :11], w.gen_v()[2, :, :11])
