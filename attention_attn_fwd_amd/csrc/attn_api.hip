@@ -44,21 +44,31 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   return dp.err;
 }
 
+// A failed launch is reported through the status code; the runtime's
+// per-thread error state it set is consumed so it does not surface later in
+// the caller's unrelated HIP calls.
+int launch_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  (void)hipGetLastError();
+  return ATTN_ERR_HIP;
+}
+
 bool supported_width(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Keys per split for the decode path: the smallest power of two >= 128 that
-// keeps the grid within about 8 workgroups per CU at full length, capped at
-// 4096 keys.  ATTN_FWD_SPLIT_CHUNK (a multiple of 128) overrides it.
+// Keys per split for the decode path: the smallest power of two >= 256 that
+// keeps the grid within 16384 single-wave workgroups at full length (a few
+// dozen per CU, so the uneven lengths of a batch balance out), capped at 4096
+// keys.  ATTN_FWD_SPLIT_CHUNK (a multiple of 32) overrides it.
 int split_chunk(int B, int Hkv, int K) {
   if (const char* e = std::getenv("ATTN_FWD_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v >= kDecodeChunkAlign && v % kDecodeChunkAlign == 0) return v;
   }
   const int64_t groups = (int64_t)B * Hkv;
-  const int64_t target = 2048;
-  int ch = kDecodeChunkAlign;
+  const int64_t target = 16384;
+  int ch = 256;
   while (ch < 4096 && groups * ((K + ch - 1) / ch) > target) ch *= 2;
   return ch;
 }
@@ -113,8 +123,8 @@ int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* 
   p.scale = scale;
   p.rows = p.group * Q;
 
-  if (!bf16) return launch_fwd_f32(p, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-  if (plan.path == 1) return launch_prefill_bf16(p, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (!bf16) return launch_status(launch_fwd_f32(p, stream));
+  if (plan.path == 1) return launch_status(launch_prefill_bf16(p, stream));
 
   // Split-KV decode: scratch from the device's stream-ordered pool.
   p.chunk = plan.split_chunk;
@@ -132,15 +142,15 @@ int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* 
       return ATTN_ERR_OOM;
   }
   float* wsf = static_cast<float*>(ws);
-  p.ws_m = wsf;
-  p.ws_l = wsf + parts;
-  p.ws_acc = wsf + 2 * parts;
-  const hipError_t e = launch_decode_bf16(p, stream);
+  p.ws_acc = wsf;  // [parts][Dv] first: 16-byte aligned rows
+  p.ws_m = wsf + parts * Dv;
+  p.ws_l = p.ws_m + parts;
+  const int launched = launch_status(launch_decode_bf16(p, stream));
   if (ws) {
     const hipError_t ef = hipFreeAsync(ws, stream);
-    if (e == hipSuccess && ef != hipSuccess) return ATTN_ERR_HIP;
+    if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;
   }
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return launched;
 }
 
 }  // namespace

@@ -15,11 +15,10 @@ constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 128 query rows
 constexpr int kPrefillBN = 64;                                   // keys per block
 
-// Split-KV decode: 4 waves, each consuming 32-key sub-blocks; chunks are
-// multiples of 128 keys so every sub-block lies inside one chunk.
-constexpr int kDecodeWaves = 4;
+// Split-KV decode: single-wave workgroups streaming 32-key sub-blocks; chunks
+// are multiples of 32 keys so every sub-block lies inside one chunk.
 constexpr int kDecodeSub = 32;
-constexpr int kDecodeChunkAlign = kDecodeWaves * kDecodeSub;
+constexpr int kDecodeChunkAlign = kDecodeSub;
 constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
 constexpr int kDecodeMaxQ = 4;
 
@@ -110,6 +109,25 @@ __device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_su
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Online softmax with a lazy reference: a row keeps its reference max m (log2
+// units) until a block's max exceeds it by more than kLazyRescale, so the
+// weights 2^(s*c - m) stay <= 2^kLazyRescale and the row sum and accumulators
+// are rescaled only when some lane of the wave needs it.  The result is the
+// same softmax: numerator and denominator share the reference.
+constexpr float kLazyRescale = 8.f;
+
+// Updates m_run from the block max mb (log2 units, -inf if the block has no
+// legal key for this row).  Returns true (wave-uniform) when the caller must
+// multiply its row sum and accumulators by alpha.
+__device__ __forceinline__ bool softmax_rebase(float& m_run, float mb, float& alpha) {
+  alpha = 1.f;
+  if (!__builtin_amdgcn_ballot_w64(mb > m_run + kLazyRescale)) return false;
+  const float mnew = fmaxf(m_run, mb);
+  alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run - mnew);
+  m_run = mnew;
+  return true;
+}
+
 // Pack eight floats into bf16 (round to nearest even).
 __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
   bf16x8 r;
@@ -125,5 +143,69 @@ __device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 __device__ __forceinline__ uint4 load_u4(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS tile loads
+// ---------------------------------------------------------------------------
+// Raw buffer resource over one (batch, head) slice of `bytes` bytes.  Offsets
+// at or beyond `bytes` read as zero, which is how key rows past K_b and
+// channel chunks past D are zero-filled without branches.  Word 3 selects a
+// 32-bit data format, as raw buffer loads on gfx9-class parts require.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+
+// Descriptor words: 48-bit base, stride 0 (raw), num_records = bytes.
+__device__ __forceinline__ rsrc_t slice_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return rsrc_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, kRsrcWord3};
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const ATTN_LDS void*)(p);
+}
+
+// One wave-wide 16-byte-per-lane load straight into LDS: lane l's 16 bytes
+// land at LDS offset lds_wave_base + 16*l (lds_wave_base is wave-uniform).
+// Issued as inline asm on purpose: the compiler then inserts no waits of its
+// own for these loads (it cannot tell ring stages apart and would wait for
+// every load in flight before any LDS read); the kernels wait explicitly with
+// wait_vmcnt, counting only these loads, which are the only vector-memory
+// operations inside their loops.  m0 is set right before the load; the
+// compiler never keeps a value of its own in m0 across code on this target.
+__device__ __forceinline__ void load_lds16(rsrc_t rs, uint32_t lds_wave_base, uint32_t voffset) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voffset), "s"(rs)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Makes the compiler treat `x` as produced here, after an explicit wait, so it
+// inserts no further waits for the load that produced it.
+template <typename T>
+__device__ __forceinline__ void launder(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Waits until at most N vector-memory operations of this wave are in flight
+// (direct-to-LDS loads count until their data is in LDS).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS tiles of rows of NCH 16-byte chunks are stored XOR-swizzled: chunk c of
+// row r sits at chunk position c ^ swz(r).  K tiles use swz(r) = r % NCH so the
+// 16 rows of a 16-byte MFMA-fragment read hit distinct banks; V tiles use
+// swz(r) = 2r % NCH so the 4-row, 32-byte pieces of a transposed read do.
+template <int NCH>
+__device__ __forceinline__ int swz_k(int row) { return row & (NCH - 1); }
+template <int NCH>
+__device__ __forceinline__ int swz_v(int row) { return (2 * row) & (NCH - 1); }
 
 }  // namespace attn

@@ -6,19 +6,20 @@
 // of that state, which is what the combine pass does, and that one kv-head
 // serves Hq/Hkv query heads; section 4 notes that a single query row cannot
 // fill a matrix atom.  Hence:
-//   * one workgroup per (chunk of keys, kv-head, batch); the g*Q query rows
-//     of the kv-head's group are packed as the 16-wide N side of
-//     v_mfma_f32_16x16x32_bf16, keys on the M side, so K and V are read from
-//     HBM once per (batch, kv-head);
-//   * the 4 waves of a workgroup take interleaved 32-key sub-blocks of the
-//     chunk; K fragments go straight from HBM to registers in MFMA layout, V
-//     goes through a wave-private LDS tile and is read back transposed with
-//     ds_read_b64_tr_b16; the next sub-block's loads are issued before the
-//     current one is computed;
-//   * at the end the waves' states are merged in LDS in a fixed order and
-//     written as one partial (m, l, acc[Dv]) per (row, chunk);
-//   * the combine pass merges the partials of each row in chunk order, so
-//     results are bitwise reproducible (no atomics).
+//   * one single-wave workgroup per (chunk of keys, kv-head, batch); the g*Q
+//     query rows of the kv-head's group are packed as the 16-wide N side of
+//     v_mfma_f32_16x16x32_bf16 and keys are the M side, so K and V are read
+//     from HBM once per (batch, kv-head);
+//   * the chunk streams through a three-stage LDS ring of 32-key sub-blocks
+//     filled by direct buffer-to-LDS loads: while sub-block j is computed the
+//     loads of j+1 are in flight, and j+2 is issued as soon as j is consumed;
+//     rows past K_b and channels past D read as zero from the buffer range
+//     check, so the loads have no branches;
+//   * each workgroup writes one fp32 partial (m, l, acc[Dv]) per row;
+//   * the combine pass merges a row's partials in chunk order, so results are
+//     bitwise reproducible (no atomics).
+#include <mutex>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -27,13 +28,16 @@ template <int DP, int DVP, int NT>
 struct DecodeShape {
   static constexpr int KS = DP / 32;
   static constexpr int JV = DVP / 16;
-  static constexpr int VROW = DVP + 8;
+  static constexpr int KCH = DP / 8;            // 16-byte chunks per K row
   static constexpr int VCH = DVP / 8;
-  static constexpr int VLOADS = kDecodeSub * VCH / 64;  // per lane per sub-block
-  static constexpr int ROWS = 16 * NT;
-  static constexpr int VS_BYTES = kDecodeWaves * kDecodeSub * VROW * 2;
-  static constexpr int BUF_BYTES = ROWS * DVP * 4;
-  static constexpr int SMEM_BYTES = VS_BYTES > BUF_BYTES ? VS_BYTES : BUF_BYTES;
+  static constexpr int KROWB = DP * 2;          // LDS bytes per K row
+  static constexpr int VROWB = DVP * 2;
+  static constexpr int K_STAGE = kDecodeSub * KROWB;
+  static constexpr int V_STAGE = kDecodeSub * VROWB;
+  static constexpr int STAGE = K_STAGE + V_STAGE;
+  static constexpr int K_LOADS = K_STAGE / 1024;  // wave-wide 1 KiB loads per stage
+  static constexpr int V_LOADS = V_STAGE / 1024;
+  static constexpr int LOADS = K_LOADS + V_LOADS;
 };
 
 // Union of the legal key ranges of all rows of one (batch, kv-head) group:
@@ -45,15 +49,25 @@ __device__ __forceinline__ void group_key_range(int Kb, int Q, int W, int* lo, i
 }
 
 template <int DP, int DVP, int NT>
-__global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
+__global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   using S = DecodeShape<DP, DVP, NT>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::SMEM_BYTES];
-  __shared__ float red_m[kDecodeWaves][S::ROWS];
-  __shared__ float red_l[kDecodeWaves][S::ROWS];
+  // The three ring stages are separate LDS objects (see the unrolled loop below).
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[S::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char stage2[S::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int chunk = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  // Persistent grid: each workgroup walks items (chunk, batch, kv-head) with
+  // the chunk index slowest, so every workgroup sees every chunk level and the
+  // uneven lengths of a batch spread evenly; items past a sequence's end cost
+  // one cached length lookup.
+  const int groups = p.B * p.Hkv;
+  const int n_items = p.n_splits * groups;
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  const int chunk = item / groups;
+  const int b = (item - chunk * groups) / p.Hkv;
+  const int kh = item - chunk * groups - b * p.Hkv;
   const int Kb = clamp_len(p.seqlens, b, p.K);
   const int Q = p.Q, W = p.window, delta = Kb - Q;
   int lo_u, hi_u;
@@ -61,11 +75,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
   const int cs = chunk * p.chunk;
   const int ce = min(cs + p.chunk, hi_u);
   const int st = max(cs, lo_u);
-  if (st >= ce) return;  // the combine pass never reads this split
+  if (st >= ce) continue;  // the combine pass never reads this split
+  // The previous item's reads of the ring have returned before it is refilled.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + kh) * p.K * p.D;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + kh) * p.K * p.Dv;
-  uint16_t* vs = reinterpret_cast<uint16_t*>(smem) + wave * kDecodeSub * S::VROW;
+  const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
+  const rsrc_t krs =
+      slice_rsrc(static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D, (uint32_t)Kb * p.D * 2);
+  const rsrc_t vrs =
+      slice_rsrc(static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv, (uint32_t)Kb * p.Dv * 2);
+  const int dch = p.D / 8, dvch = p.Dv / 8;
   const float c = p.scale_log2;
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
@@ -86,6 +105,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
       qf[t][s] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  // Q is in registers before any direct load is issued.
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) launder(qf[t][s]);
 
   float m_run[NT], l_run[NT];
   f32x4 acc[S::JV][NT];
@@ -97,42 +122,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     for (int j = 0; j < S::JV; ++j) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int j0 = (st - cs) / kDecodeSub;
-  const int j1 = (ce - cs + kDecodeSub - 1) / kDecodeSub;
-
-  uint4 kcur[2][S::KS], vcur[S::VLOADS];
-  auto gload = [&](int j, uint4 (&kr)[2][S::KS], uint4 (&vr)[S::VLOADS]) {
+  // Issue the direct loads of sub-block j into the ring stage at `kst`.
+  auto issue = [&](int j, unsigned char* kst) {
     const int kb0 = cs + j * kDecodeSub;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int key = kb0 + 16 * i + l16;
-#pragma unroll
-      for (int s = 0; s < S::KS; ++s) {
-        const int col = 32 * s + 8 * g4;
-        kr[i][s] = (key < Kb && col < p.D) ? load_u4(kg + (int64_t)key * p.D + col) : zero_u4();
-      }
+    for (int i = 0; i < S::K_LOADS; ++i) {
+      const int off = i * 1024 + 16 * lane;
+      const int row = off / S::KROWB, ch = ((off % S::KROWB) >> 4) ^ swz_k<S::KCH>(row);
+      const uint32_t vo = ch < dch ? ((uint32_t)(kb0 + row) * p.D + ch * 8) * 2 : kOutOfRange;
+      load_lds16(krs, lds_offset(kst) + i * 1024, vo);
     }
+    unsigned char* vst = kst + S::K_STAGE;
 #pragma unroll
-    for (int i = 0; i < S::VLOADS; ++i) {
-      const int idx = lane + 64 * i, r = idx / S::VCH, ch = idx % S::VCH, key = kb0 + r;
-      vr[i] = (key < Kb && ch * 8 < p.Dv) ? load_u4(vg + (int64_t)key * p.Dv + ch * 8) : zero_u4();
+    for (int i = 0; i < S::V_LOADS; ++i) {
+      const int off = i * 1024 + 16 * lane;
+      const int row = off / S::VROWB, ch = ((off % S::VROWB) >> 4) ^ swz_v<S::VCH>(row);
+      const uint32_t vo = ch < dvch ? ((uint32_t)(kb0 + row) * p.Dv + ch * 8) * 2 : kOutOfRange;
+      load_lds16(vrs, lds_offset(vst) + i * 1024, vo);
     }
   };
 
-  int j = j0 + wave;
-  if (j < j1) gload(j, kcur, vcur);
-  for (; j < j1; j += kDecodeWaves) {
-    // Stage this sub-block's V tile in the wave-private LDS tile.
-#pragma unroll
-    for (int i = 0; i < S::VLOADS; ++i) {
-      const int idx = lane + 64 * i, r = idx / S::VCH, ch = idx % S::VCH;
-      *reinterpret_cast<uint4*>(&vs[r * S::VROW + ch * 8]) = vcur[i];
-    }
-    uint4 knext[2][S::KS], vnext[S::VLOADS];
-    const bool more = j + kDecodeWaves < j1;
-    if (more) gload(j + kDecodeWaves, knext, vnext);
+  const int j0 = (st - cs) / kDecodeSub;
+  const int j1 = (ce - cs + kDecodeSub - 1) / kDecodeSub;
+  issue(j0, stage0);
+  if (j0 + 1 < j1) issue(j0 + 1, stage1);
 
+  // One sub-block: wait for its stage `kst`, compute it, and issue sub-block
+  // j + 2 into `nxt`, the stage read one step earlier.
+  auto step = [&](int j, const unsigned char* kst, unsigned char* nxt) {
+    if (j + 1 < j1) wait_vmcnt<S::LOADS>();
+    else wait_vmcnt<0>();
+    const unsigned char* vst = kst + S::K_STAGE;
     const int kb0 = cs + j * kDecodeSub;
+
     f32x4 sacc[2][NT];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -142,7 +164,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     for (int s = 0; s < S::KS; ++s) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, kcur[i][s]);
+        const int row = 16 * i + l16;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            kst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
 #pragma unroll
         for (int t = 0; t < NT; ++t) sacc[i][t] = mfma16x16x32(a, qf[t][s], sacc[i][t]);
       }
@@ -152,8 +176,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
     if (!full) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int rr = 16 * t + l16;
-        const int pq = (rr % Q) + delta;
+        const int pq = ((16 * t + l16) % Q) + delta;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -175,97 +198,76 @@ __global__ __launch_bounds__(256) void decode_split_kernel(Params p) {
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[i][t][r]);
       mx = group4_max(mx);
       const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const float mnew = fmaxf(m_run[t], mb);
-      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
-      m_run[t] = mnew;
+      float alpha;
+      if (softmax_rebase(m_run[t], mb, alpha)) {
+        l_run[t] *= alpha;
+#pragma unroll
+        for (int jv = 0; jv < S::JV; ++jv) acc[jv][t] *= alpha;
+      }
+      const float mref = m_run[t];
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float sv = sacc[i][t][r];
-          float e = fast_exp2(fmaf(sv, c, -mnew));
+          float e = fast_exp2(fmaf(sv, c, -mref));
           if (!full) e = (sv == -INFINITY) ? 0.f : e;
           sacc[i][t][r] = e;
           rs += e;
         }
       }
-      l_run[t] = l_run[t] * alpha + rs;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int jv = 0; jv < S::JV; ++jv) acc[jv][t] *= alpha;
-      }
+      l_run[t] += rs;
       pf[t] = pack_bf16x8(sacc[0][t], sacc[1][t]);
     }
-    // LDS operations of one wave complete in issue order; this keeps the
-    // compiler from moving the tile stores past the transposed reads.
-    asm volatile("" ::: "memory");
+    // O^T += V^T P^T: contraction index e maps to key 4*g4 + e (e < 4) or
+    // 16 + 4*g4 + e - 4, the S^T register layout; V^T comes from the
+    // transposed read of 4-row pieces of the swizzled V tile.
 #pragma unroll
     for (int jv = 0; jv < S::JV; ++jv) {
-      const uint16_t* vlo = &vs[(4 * g4 + (l16 >> 2)) * S::VROW + 16 * jv + 4 * (l16 & 3)];
-      const bf16x8 va = concat_bf16x4(lds_read_tr16(vlo), lds_read_tr16(vlo + 16 * S::VROW));
+      const int row = 4 * g4 + (l16 >> 2);
+      const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+      const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
+      const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
+      const bf16x8 va = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
+                                      lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(va, pf[t], acc[jv][t]);
     }
-    asm volatile("" ::: "memory");
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int s = 0; s < S::KS; ++s) kcur[i][s] = knext[i][s];
-#pragma unroll
-      for (int i = 0; i < S::VLOADS; ++i) vcur[i] = vnext[i];
+    if (j + 2 < j1) {
+      // The reads of `nxt` (previous step) have all returned before its refill.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(j + 2, nxt);
     }
+  };
+  // Unrolled by three so every access names one stage statically.
+  for (int j = j0; j < j1; j += 3) {
+    step(j, stage0, stage2);
+    if (j + 1 < j1) step(j + 1, stage1, stage0);
+    if (j + 2 < j1) step(j + 2, stage2, stage1);
   }
 
-  // Merge the four waves' states in a fixed order.
-  float lt[NT];
+  // One partial per (row, chunk): m in log2 units, l = sum of 2^(s*c - m), unnormalised acc.
+  const int64_t split = kv_slice * p.n_splits + chunk;
+  const int R = p.rows;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    lt[t] = group4_sum(l_run[t]);
-    if (g4 == 0) {
-      red_m[wave][16 * t + l16] = m_run[t];
-      red_l[wave][16 * t + l16] = lt[t];
-    }
-  }
-  __syncthreads();
-  float* buf = reinterpret_cast<float*>(smem);  // [ROWS][DVP], reuses the V tiles
+    const float lt = group4_sum(l_run[t]);
+    const int rr = 16 * t + l16;
+    if (rr < R) {
+      const int64_t part = split * R + rr;
+      if (g4 == 0) {
+        p.ws_m[part] = m_run[t];
+        p.ws_l[part] = lt;
+      }
 #pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int rr = 16 * t + l16;
-        float M = red_m[0][rr];
-#pragma unroll
-        for (int u = 1; u < kDecodeWaves; ++u) M = fmaxf(M, red_m[u][rr]);
-        const float f = (m_run[t] == -INFINITY) ? 0.f : fast_exp2(m_run[t] - M);
-#pragma unroll
-        for (int jv = 0; jv < S::JV; ++jv) {
-          f32x4* dst = reinterpret_cast<f32x4*>(&buf[rr * DVP + 16 * jv + 4 * g4]);
-          const f32x4 v = acc[jv][t] * f;
-          *dst = (w == 0) ? v : (*dst + v);
-        }
+      for (int jv = 0; jv < S::JV; ++jv) {
+        const int dv = 16 * jv + 4 * g4;
+        if (dv < p.Dv) *reinterpret_cast<f32x4*>(p.ws_acc + part * p.Dv + dv) = acc[jv][t];
       }
     }
-    __syncthreads();
   }
-  const int64_t split = ((int64_t)b * p.Hkv + kh) * p.n_splits + chunk;
-  const int R = p.rows;
-  for (int rr = tid; rr < R; rr += 256) {
-    float M = red_m[0][rr];
-    for (int u = 1; u < kDecodeWaves; ++u) M = fmaxf(M, red_m[u][rr]);
-    float L = 0.f;
-    for (int u = 0; u < kDecodeWaves; ++u)
-      if (red_m[u][rr] != -INFINITY) L += red_l[u][rr] * fast_exp2(red_m[u][rr] - M);
-    p.ws_m[split * R + rr] = M;
-    p.ws_l[split * R + rr] = L;
-  }
-  float* wacc = p.ws_acc + split * R * p.Dv;
-  for (int idx = tid; idx < R * p.Dv; idx += 256) {
-    const int rr = idx / p.Dv, dv = idx % p.Dv;
-    wacc[idx] = buf[rr * DVP + dv];
-  }
+  }  // items
 }
 
 // One wave per output row (b, h, q): merge the row's partials in chunk order.
@@ -309,14 +311,41 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   if (lane == 0) p.lse[row_id] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Workgroups of the split kernel that fit on the current device at once (CU
+// count times workgroups per CU), computed once per device and instantiation;
+// 0 if the runtime cannot say.
+template <int DP, int DVP, int NT>
+static int decode_slots() {
+  constexpr int kMaxDev = 64;
+  static std::once_flag once[kMaxDev];
+  static int slots[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  std::call_once(once[dev], [dev]() {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), 64, 0) != hipSuccess)
+      slots[dev] = 0;
+    else
+      slots[dev] = cus * (per_cu > 0 ? per_cu : 1);
+  });
+  return slots[dev];
+}
+
 template <int DP, int DVP, int NT>
 static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   Params arg = p;
   void* args[] = {&arg};
-  const dim3 grid((unsigned)p.n_splits, (unsigned)p.Hkv, (unsigned)p.B);
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), grid, dim3(256),
-                                 args, 0, stream);
-  if (e != hipSuccess) return e;
+  // With K == 0 there is no split: the combine pass alone writes 0 / -inf.
+  if (p.n_splits > 0) {
+    const int64_t items = (int64_t)p.n_splits * p.Hkv * p.B;
+    const int slots = decode_slots<DP, DVP, NT>();
+    const dim3 grid((unsigned)(slots > 0 && slots < items ? slots : items));
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), grid,
+                                         dim3(64), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   const int64_t rows = (int64_t)p.B * p.Hq * p.Q;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
   return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel), cgrid, dim3(256), args, 0, stream);

@@ -6,16 +6,24 @@
 //
 // Mapping on CDNA4:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//     owns 32 rows as two 16-column MFMA tiles, Q held in registers;
-//   * K/V blocks of 64 keys are staged in LDS, the next block's global loads
-//     are issued into registers before the current block is computed;
+//     owns 32 rows as two 16-column MFMA tiles, Q held in registers; two
+//     workgroups share a CU, so one's softmax overlaps the other's MFMAs;
+//   * K/V blocks of 64 keys go HBM -> LDS by direct buffer loads into a
+//     two-stage ring: block j+1 is in flight while block j is computed, one
+//     barrier per block; rows past K_b and channels past D read as zero from
+//     the buffer range check;
+//   * tiles are XOR-swizzled in LDS so the 16-byte K fragment reads and the
+//     transposed V reads are free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane holds 16 keys of
 //     one query column and the row max/sum is in-lane plus two permlane swaps;
 //   * P^T stays in the S^T register layout and feeds O^T = V^T P^T directly;
 //     V^T fragments come from row-major LDS through ds_read_b64_tr_b16;
 //   * masks are evaluated only on blocks that straddle the causal diagonal, a
 //     window edge or the sequence end; blocks no row of a wave can see are
-//     skipped by that wave.
+//     skipped by that wave;
+//   * tiles are ordered heaviest causal tile first, and the (batch, kv-head)
+//     groups are dealt to the 8 XCDs so the query heads sharing a kv-head run
+//     on one XCD and reuse its L2.
 #include "attn_internal.h"
 
 namespace attn {
@@ -24,34 +32,54 @@ template <int DP, int DVP>
 struct PrefillShape {
   static constexpr int KS = DP / 32;        // 32-deep k-steps of Q.K
   static constexpr int JV = DVP / 16;       // 16-wide dv tiles of O^T
-  static constexpr int KROW = DP + 8;       // LDS row pitch of K (elements)
-  static constexpr int VROW = DVP + 8;      // LDS row pitch of V (elements)
   static constexpr int KCH = DP / 8;        // 16-byte chunks per K row
   static constexpr int VCH = DVP / 8;
-  static constexpr int KLOADS = kPrefillBN * KCH / 256;
-  static constexpr int VLOADS = kPrefillBN * VCH / 256;
-  static_assert(kPrefillBN * KCH % 256 == 0 && kPrefillBN * VCH % 256 == 0, "load split");
+  static constexpr int KROWB = DP * 2;      // LDS bytes per K row
+  static constexpr int VROWB = DVP * 2;
+  static constexpr int K_TILE = kPrefillBN * KROWB;
+  static constexpr int V_TILE = kPrefillBN * VROWB;
+  static constexpr int STAGE = K_TILE + V_TILE;
+  static constexpr int K_LOADS = K_TILE / 4096;  // 16-byte loads per thread per block
+  static constexpr int V_LOADS = V_TILE / 4096;
+  static_assert(K_TILE % 4096 == 0 && V_TILE % 4096 == 0, "load split");
 };
 
+// Block index -> (query tile, batch, head).  When the (batch, kv-head) groups
+// divide evenly over the 8 XCDs (workgroup i runs on XCD i % 8), each XCD gets
+// whole groups and walks their query tiles heaviest first; otherwise the
+// order is heaviest tile first with heads fastest.
+__device__ __forceinline__ void prefill_tile(const Params& p, int n_qt, int* qt, int* b, int* h) {
+  const int x = blockIdx.x;
+  const int groups = p.B * p.Hkv;
+  if ((groups & 7) == 0) {
+    const int xcd = x & 7, slot = x >> 3;
+    const int per_qt = (groups >> 3) * p.group;
+    const int qrank = slot / per_qt, rem = slot - qrank * per_qt;
+    const int grp = (rem / p.group) * 8 + xcd;
+    *b = grp / p.Hkv;
+    *h = (grp - *b * p.Hkv) * p.group + rem % p.group;
+    *qt = n_qt - 1 - qrank;
+  } else {
+    *h = x % p.Hq;
+    const int y = x / p.Hq;
+    *b = y % p.B;
+    *qt = n_qt - 1 - y / p.B;
+  }
+}
+
 template <int DP, int DVP>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   using S = PrefillShape<DP, DVP>;
   constexpr int BN = kPrefillBN;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * S::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * S::VROW];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // Heaviest causal tiles first: the query tile index is the slowest digit.
   const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
-  int x = blockIdx.x;
-  const int h = x % p.Hq;
-  x /= p.Hq;
-  const int b = x % p.B;
-  x /= p.B;
-  const int qt = n_qt - 1 - x;
+  int qt, b, h;
+  prefill_tile(p, n_qt, &qt, &b, &h);
   const int kh = h / p.group;
 
   const int Kb = clamp_len(p.seqlens, b, p.K);
@@ -60,16 +88,18 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
   const int q0 = qt * kPrefillBM;
   const int q_end = min(q0 + kPrefillBM, p.Q);
 
-  int kv_hi = min(Kb, q_end - 1 + delta + 1);
-  int kv_lo = W > 0 ? max(0, q0 + delta - W + 1) : 0;
+  const int kv_hi = min(Kb, q_end - 1 + delta + 1);
+  const int kv_lo = W > 0 ? max(0, q0 + delta - W + 1) : 0;
   const int jb0 = kv_lo / BN;
   const int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
 
+  const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Q * p.D;
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + kh) * p.K * p.D;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + kh) * p.K * p.Dv;
+  const rsrc_t krs = slice_rsrc(static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D, (uint32_t)Kb * p.D * 2);
+  const rsrc_t vrs = slice_rsrc(static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv, (uint32_t)Kb * p.Dv * 2);
   uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Q * p.Dv;
   float* lg = p.lse + ((int64_t)b * p.Hq + h) * p.Q;
+  const int dch = p.D / 8, dvch = p.Dv / 8;
 
   const int qw0 = q0 + wave * kPrefillRowsPerWave;
   const bool wave_has_rows = qw0 < p.Q;
@@ -91,6 +121,12 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
       qf[t][s] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  // Q is in registers before any direct load is issued.
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) launder(qf[t][s]);
 
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
@@ -98,41 +134,41 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
 #pragma unroll
   for (int j = 0; j < S::JV; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 kreg[S::KLOADS], vreg[S::VLOADS];
-  auto gload = [&](int jb) {
+  // Direct loads of block jb into ring stage `stg`: each wave-wide load fills
+  // 1 KiB of the tile; lane l's 16 bytes land at position l of it, so the lane
+  // fetches the global chunk that the swizzle places there.
+  const uint32_t ring_base = lds_offset(ring);
+  auto issue = [&](int jb, int stg) {
     const int kb0 = jb * BN;
+    const uint32_t kbase = ring_base + stg * S::STAGE;
 #pragma unroll
-    for (int i = 0; i < S::KLOADS; ++i) {
-      const int idx = tid + 256 * i, r = idx / S::KCH, ch = idx % S::KCH, key = kb0 + r;
-      kreg[i] = (key < Kb && ch * 8 < p.D) ? load_u4(kg + (int64_t)key * p.D + ch * 8) : zero_u4();
+    for (int i = 0; i < S::K_LOADS; ++i) {
+      const int byte0 = (i * kPrefillWaves + wave) * 1024;
+      const int off = byte0 + 16 * lane;
+      const int row = off / S::KROWB, ch = ((off % S::KROWB) >> 4) ^ swz_k<S::KCH>(row);
+      const uint32_t vo = ch < dch ? ((uint32_t)(kb0 + row) * p.D + ch * 8) * 2 : kOutOfRange;
+      load_lds16(krs, kbase + __builtin_amdgcn_readfirstlane(byte0), vo);
     }
+    const uint32_t vbase = kbase + S::K_TILE;
 #pragma unroll
-    for (int i = 0; i < S::VLOADS; ++i) {
-      const int idx = tid + 256 * i, r = idx / S::VCH, ch = idx % S::VCH, key = kb0 + r;
-      vreg[i] = (key < Kb && ch * 8 < p.Dv) ? load_u4(vg + (int64_t)key * p.Dv + ch * 8) : zero_u4();
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < S::KLOADS; ++i) {
-      const int idx = tid + 256 * i, r = idx / S::KCH, ch = idx % S::KCH;
-      *reinterpret_cast<uint4*>(&Ks[r * S::KROW + ch * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::VLOADS; ++i) {
-      const int idx = tid + 256 * i, r = idx / S::VCH, ch = idx % S::VCH;
-      *reinterpret_cast<uint4*>(&Vs[r * S::VROW + ch * 8]) = vreg[i];
+    for (int i = 0; i < S::V_LOADS; ++i) {
+      const int byte0 = (i * kPrefillWaves + wave) * 1024;
+      const int off = byte0 + 16 * lane;
+      const int row = off / S::VROWB, ch = ((off % S::VROWB) >> 4) ^ swz_v<S::VCH>(row);
+      const uint32_t vo = ch < dvch ? ((uint32_t)(kb0 + row) * p.Dv + ch * 8) * 2 : kOutOfRange;
+      load_lds16(vrs, vbase + __builtin_amdgcn_readfirstlane(byte0), vo);
     }
   };
 
-  if (jb0 < jb1) {
-    gload(jb0);
-    lstore();
-  }
+  if (jb0 < jb1) issue(jb0, 0);
+  wait_vmcnt<0>();
   __syncthreads();
 
   for (int jb = jb0; jb < jb1; ++jb) {
-    if (jb + 1 < jb1) gload(jb + 1);
+    const int stg = (jb - jb0) & 1;
+    if (jb + 1 < jb1) issue(jb + 1, stg ^ 1);
+    const unsigned char* kst = ring + stg * S::STAGE;
+    const unsigned char* vst = kst + S::K_TILE;
     const int kb0 = jb * BN;
     const int pw_first = qw0 + delta, pw_last = qw_last + delta;
     const bool skip = !wave_has_rows || kb0 > pw_last || kb0 >= Kb || (W > 0 && kb0 + BN - 1 < pw_first - W + 1);
@@ -145,7 +181,9 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
       for (int s = 0; s < S::KS; ++s) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(16 * i + l16) * S::KROW + 32 * s + 8 * g4]);
+          const int row = 16 * i + l16;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              kst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
           sacc[i][0] = mfma16x16x32(a, qf[0][s], sacc[i][0]);
           sacc[i][1] = mfma16x16x32(a, qf[1][s], sacc[i][1]);
         }
@@ -175,26 +213,26 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
           for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[i][t][r]);
         mx = group4_max(mx);
         const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
-        const float mnew = fmaxf(m_run[t], mb);
-        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
-        m_run[t] = mnew;
+        float alpha;
+        if (softmax_rebase(m_run[t], mb, alpha)) {
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
+        }
+        const float mref = m_run[t];
         float rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float sv = sacc[i][t][r];
-            float e = fast_exp2(fmaf(sv, c, -mnew));
+            float e = fast_exp2(fmaf(sv, c, -mref));
             if (!full) e = (sv == -INFINITY) ? 0.f : e;
             sacc[i][t][r] = e;
             rs += e;
           }
         }
-        l_run[t] = l_run[t] * alpha + rs;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-          for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
-        }
+        l_run[t] += rs;
         pf[t][0] = pack_bf16x8(sacc[0][t], sacc[1][t]);
         pf[t][1] = pack_bf16x8(sacc[2][t], sacc[3][t]);
       }
@@ -203,17 +241,21 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(Params p) {
       // the S^T register layout; the V^T fragment is read in the same order.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        const int row = 32 * kk + 4 * g4 + (l16 >> 2);
 #pragma unroll
         for (int j = 0; j < S::JV; ++j) {
-          const uint16_t* vlo = &Vs[(32 * kk + 4 * g4 + (l16 >> 2)) * S::VROW + 16 * j + 4 * (l16 & 3)];
-          const bf16x8 va = concat_bf16x4(lds_read_tr16(vlo), lds_read_tr16(vlo + 16 * S::VROW));
+          const int ch = 2 * j + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+          const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
+          const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
+          const bf16x8 va = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
+                                          lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
           acc[j][0] = mfma16x16x32(va, pf[0][kk], acc[j][0]);
           acc[j][1] = mfma16x16x32(va, pf[1][kk], acc[j][1]);
         }
       }
     }
-    __syncthreads();
-    if (jb + 1 < jb1) lstore();
+    // Block jb+1 has landed for every wave, and every wave is done with stage stg.
+    wait_vmcnt<0>();
     __syncthreads();
   }
 

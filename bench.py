@@ -130,8 +130,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["step", "prefill", "decode"], default="step",
-                    help="time the whole step (default) or one of its two calls alone (for profiling)")
+    ap.add_argument("--workload", choices=["step", "prefill", "decode", "copy"], default="step",
+                    help="time the whole step (default), one of its two calls alone (for profiling), or a "
+                         "plain 1 GiB device copy (to calibrate the HBM byte counters)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -150,6 +151,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "copy":
+        # A plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch calibrate the counters.
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": nbytes,
+                          "bytes_written_per_dispatch": nbytes, "dispatches": args.warmup + args.steps}))
+        return
     prefill_w, decode_w = inputs.config(3), inputs.config(5)
     probs = []
     if args.workload in ("step", "prefill"):
