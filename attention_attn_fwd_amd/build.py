@@ -6,7 +6,8 @@
   libattn_inputs.so  the seeded input generator (csrc/inputs.c, gcc + OpenMP)
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
-off (-Xclang -target-feature -Xclang -packed-fp32-ops).
+off (-Xclang -target-feature -Xclang -packed-fp32-ops) and with MFMA results
+kept in VGPRs (-mllvm -amdgpu-mfma-vgpr-form).
 """
 from __future__ import annotations
 
@@ -28,6 +29,9 @@ HIP_SOURCES = ["attn_api.hip", "prefill_bf16.hip", "decode_bf16.hip", "fwd_f32.h
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the accumulators are also rescaled by
+    # VALU code, and the AGPR form copies them back and forth every block.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -58,16 +58,17 @@ bool supported_width(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Keys per split for the decode path: the smallest power of two >= 256 that
-// keeps the grid within 16384 single-wave workgroups at full length (a few
-// dozen per CU, so the uneven lengths of a batch balance out), capped at 4096
-// keys.  ATTN_FWD_SPLIT_CHUNK (a multiple of 32) overrides it.
+// keeps the grid within 8192 single-wave workgroups at full length (dozens per
+// CU, so the uneven lengths of a batch balance out, while each workgroup
+// streams long enough to amortise its start), capped at 4096 keys.
+// ATTN_FWD_SPLIT_CHUNK (a multiple of 32) overrides it.
 int split_chunk(int B, int Hkv, int K) {
   if (const char* e = std::getenv("ATTN_FWD_SPLIT_CHUNK")) {
     const int v = std::atoi(e);
     if (v >= kDecodeChunkAlign && v % kDecodeChunkAlign == 0) return v;
   }
   const int64_t groups = (int64_t)B * Hkv;
-  const int64_t target = 16384;
+  const int64_t target = 8192;
   int ch = 256;
   while (ch < 4096 && groups * ((K + ch - 1) / ch) > target) ch *= 2;
   return ch;

@@ -10,7 +10,7 @@
 //     query rows of the kv-head's group are packed as the 16-wide N side of
 //     v_mfma_f32_16x16x32_bf16 and keys are the M side, so K and V are read
 //     from HBM once per (batch, kv-head);
-//   * the chunk streams through a three-stage LDS ring of 32-key sub-blocks
+//   * the chunk streams through a two-stage LDS ring of 32-key sub-blocks
 //     filled by direct buffer-to-LDS loads: while sub-block j is computed the
 //     loads of j+1 are in flight, and j+2 is issued as soon as j is consumed;
 //     rows past K_b and channels past D read as zero from the buffer range
@@ -18,8 +18,6 @@
 //   * each workgroup writes one fp32 partial (m, l, acc[Dv]) per row;
 //   * the combine pass merges a row's partials in chunk order, so results are
 //     bitwise reproducible (no atomics).
-#include <mutex>
-
 #include "attn_internal.h"
 
 namespace attn {
@@ -51,19 +49,35 @@ __device__ __forceinline__ void group_key_range(int Kb, int Q, int W, int* lo, i
 template <int DP, int DVP, int NT>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   using S = DecodeShape<DP, DVP, NT>;
-  // The three ring stages are separate LDS objects (see the unrolled loop below).
-  __shared__ __attribute__((aligned(16))) unsigned char stage0[S::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stage1[S::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char stage2[S::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Persistent grid: each workgroup walks items (chunk, batch, kv-head) with
-  // the chunk index slowest, so every workgroup sees every chunk level and the
-  // uneven lengths of a batch spread evenly; items past a sequence's end cost
-  // one cached length lookup.
+  // Items (chunk, batch, kv-head) are numbered chunk-slowest, so the leading
+  // chunks of every sequence are dispatched first and the workgroups of chunks
+  // past a sequence's end (which return after one length lookup) come last.
+  // The launch has one workgroup per item; the loop also serves a smaller grid.
   const int groups = p.B * p.Hkv;
   const int n_items = p.n_splits * groups;
+
+  // This lane's byte offset, from the start of a sub-block, for each 1 KiB
+  // direct load of a stage: load i fills stage bytes [1024 i, 1024 i + 1024),
+  // lane l position l of it, which holds chunk (position ^ swizzle) of its row.
+  // Chunks past D (Dv) get an offset beyond any buffer and read as zero.
+  uint32_t koff[S::K_LOADS], voff[S::V_LOADS];
+#pragma unroll
+  for (int i = 0; i < S::K_LOADS; ++i) {
+    const int off = i * 1024 + 16 * lane;
+    const int row = off / S::KROWB, ch = ((off % S::KROWB) >> 4) ^ swz_k<S::KCH>(row);
+    koff[i] = ch < p.D / 8 ? (uint32_t)(row * p.D + ch * 8) * 2 : kOutOfRange;
+  }
+#pragma unroll
+  for (int i = 0; i < S::V_LOADS; ++i) {
+    const int off = i * 1024 + 16 * lane;
+    const int row = off / S::VROWB, ch = ((off % S::VROWB) >> 4) ^ swz_v<S::VCH>(row);
+    voff[i] = ch < p.Dv / 8 ? (uint32_t)(row * p.Dv + ch * 8) * 2 : kOutOfRange;
+  }
+
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
   const int chunk = item / groups;
   const int b = (item - chunk * groups) / p.Hkv;
@@ -80,11 +94,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
-  const rsrc_t krs =
-      slice_rsrc(static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D, (uint32_t)Kb * p.D * 2);
-  const rsrc_t vrs =
-      slice_rsrc(static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv, (uint32_t)Kb * p.Dv * 2);
-  const int dch = p.D / 8, dvch = p.Dv / 8;
+  const uint16_t* kslice = static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D;
+  const uint16_t* vslice = static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv;
   const float c = p.scale_log2;
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
@@ -122,38 +133,67 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     for (int j = 0; j < S::JV; ++j) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Issue the direct loads of sub-block j into the ring stage at `kst`.
-  auto issue = [&](int j, unsigned char* kst) {
+  // Issue the direct loads of sub-block j into ring stage `stg`.  The buffer
+  // descriptors start at the sub-block and end at K_b, so the per-lane offsets
+  // are the same for every sub-block and rows past K_b read as zero.
+  auto issue = [&](int j, int stg) {
     const int kb0 = cs + j * kDecodeSub;
+    const uint32_t rows_left = (uint32_t)(Kb - kb0);
+    const rsrc_t krs = slice_rsrc(kslice + (int64_t)kb0 * p.D, rows_left * p.D * 2);
+    const rsrc_t vrs = slice_rsrc(vslice + (int64_t)kb0 * p.Dv, rows_left * p.Dv * 2);
+    const uint32_t kst = lds_offset(ring) + stg * S::STAGE;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) {
-      const int off = i * 1024 + 16 * lane;
-      const int row = off / S::KROWB, ch = ((off % S::KROWB) >> 4) ^ swz_k<S::KCH>(row);
-      const uint32_t vo = ch < dch ? ((uint32_t)(kb0 + row) * p.D + ch * 8) * 2 : kOutOfRange;
-      load_lds16(krs, lds_offset(kst) + i * 1024, vo);
-    }
-    unsigned char* vst = kst + S::K_STAGE;
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(krs, kst + i * 1024, koff[i]);
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) {
-      const int off = i * 1024 + 16 * lane;
-      const int row = off / S::VROWB, ch = ((off % S::VROWB) >> 4) ^ swz_v<S::VCH>(row);
-      const uint32_t vo = ch < dvch ? ((uint32_t)(kb0 + row) * p.Dv + ch * 8) * 2 : kOutOfRange;
-      load_lds16(vrs, lds_offset(vst) + i * 1024, vo);
-    }
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(vrs, kst + S::K_STAGE + i * 1024, voff[i]);
   };
 
   const int j0 = (st - cs) / kDecodeSub;
   const int j1 = (ce - cs + kDecodeSub - 1) / kDecodeSub;
-  issue(j0, stage0);
-  if (j0 + 1 < j1) issue(j0 + 1, stage1);
+  issue(j0, 0);
+  if (j0 + 1 < j1) issue(j0 + 1, 1);
 
-  // One sub-block: wait for its stage `kst`, compute it, and issue sub-block
-  // j + 2 into `nxt`, the stage read one step earlier.
-  auto step = [&](int j, const unsigned char* kst, unsigned char* nxt) {
+  // Absolute position of each packed row (row rr is query rr % Q).
+  int pq[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) pq[t] = (16 * t + l16) % Q + delta;
+
+  // Sub-block j sits in stage (j - j0) % 2; once every LDS read of it has
+  // returned, sub-block j + 2 is issued into the same stage.
+  int stg = 0;
+  for (int j = j0; j < j1; ++j) {
     if (j + 1 < j1) wait_vmcnt<S::LOADS>();
     else wait_vmcnt<0>();
+    const unsigned char* kst = ring + stg * S::STAGE;
     const unsigned char* vst = kst + S::K_STAGE;
     const int kb0 = cs + j * kDecodeSub;
+
+    // Every LDS read of the sub-block is issued up front (K fragments, then the
+    // transposed V fragments), so a single wave pays the LDS latency once per
+    // step rather than once per fragment; the V reads overlap QK and softmax.
+    bf16x8 kf[2][S::KS];
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 16 * i + l16;
+        kf[i][s] = *reinterpret_cast<const bf16x8*>(kst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
+      }
+    }
+    // V^T fragments: contraction index e maps to key 4*g4 + e (e < 4) or
+    // 16 + 4*g4 + e - 4, the S^T register layout; each is two transposed reads
+    // of 4-row pieces of the swizzled V tile.
+    bf16x8 vf[S::JV];
+#pragma unroll
+    for (int jv = 0; jv < S::JV; ++jv) {
+      const int row = 4 * g4 + (l16 >> 2);
+      const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+      const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
+      const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
+      vf[jv] = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
+                             lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 sacc[2][NT];
 #pragma unroll
@@ -161,28 +201,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) sacc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < S::KS; ++s) {
+    for (int s = 0; s < S::KS; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 16 * i + l16;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            kst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sacc[i][t] = mfma16x16x32(a, qf[t][s], sacc[i][t]);
-      }
-    }
+        for (int t = 0; t < NT; ++t) sacc[i][t] = mfma16x16x32(kf[i][s], qf[t][s], sacc[i][t]);
     // Every row sees keys <= K_b - Q causally; the last row's window starts at K_b - W.
     const bool full = (kb0 + kDecodeSub - 1 <= delta) && (kb0 + kDecodeSub <= Kb) && (W <= 0 || kb0 >= Kb - W);
     if (!full) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int pq = ((16 * t + l16) % Q) + delta;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kb0 + 16 * i + 4 * g4 + r;
-            const bool legal = key <= pq && key < Kb && (W <= 0 || key > pq - W);
+            const bool legal = key <= pq[t] && key < Kb && (W <= 0 || key > pq[t] - W);
             if (!legal) sacc[i][t][r] = -INFINITY;
           }
         }
@@ -220,31 +254,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
       l_run[t] += rs;
       pf[t] = pack_bf16x8(sacc[0][t], sacc[1][t]);
     }
-    // O^T += V^T P^T: contraction index e maps to key 4*g4 + e (e < 4) or
-    // 16 + 4*g4 + e - 4, the S^T register layout; V^T comes from the
-    // transposed read of 4-row pieces of the swizzled V tile.
+    // O^T += V^T P^T.
 #pragma unroll
-    for (int jv = 0; jv < S::JV; ++jv) {
-      const int row = 4 * g4 + (l16 >> 2);
-      const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
-      const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
-      const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
-      const bf16x8 va = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
-                                      lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
+    for (int jv = 0; jv < S::JV; ++jv)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(va, pf[t], acc[jv][t]);
-    }
+      for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(vf[jv], pf[t], acc[jv][t]);
     if (j + 2 < j1) {
-      // The reads of `nxt` (previous step) have all returned before its refill.
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(j + 2, nxt);
+      issue(j + 2, stg);
     }
-  };
-  // Unrolled by three so every access names one stage statically.
-  for (int j = j0; j < j1; j += 3) {
-    step(j, stage0, stage2);
-    if (j + 1 < j1) step(j + 1, stage1, stage0);
-    if (j + 2 < j1) step(j + 2, stage2, stage1);
+    stg ^= 1;
   }
 
   // One partial per (row, chunk): m in log2 units, l = sum of 2^(s*c - m), unnormalised acc.
@@ -311,28 +330,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   if (lane == 0) p.lse[row_id] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
 
-// Workgroups of the split kernel that fit on the current device at once (CU
-// count times workgroups per CU), computed once per device and instantiation;
-// 0 if the runtime cannot say.
-template <int DP, int DVP, int NT>
-static int decode_slots() {
-  constexpr int kMaxDev = 64;
-  static std::once_flag once[kMaxDev];
-  static int slots[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  std::call_once(once[dev], [dev]() {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), 64, 0) != hipSuccess)
-      slots[dev] = 0;
-    else
-      slots[dev] = cus * (per_cu > 0 ? per_cu : 1);
-  });
-  return slots[dev];
-}
-
 template <int DP, int DVP, int NT>
 static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   Params arg = p;
@@ -340,8 +337,7 @@ static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   // With K == 0 there is no split: the combine pass alone writes 0 / -inf.
   if (p.n_splits > 0) {
     const int64_t items = (int64_t)p.n_splits * p.Hkv * p.B;
-    const int slots = decode_slots<DP, DVP, NT>();
-    const dim3 grid((unsigned)(slots > 0 && slots < items ? slots : items));
+    const dim3 grid((unsigned)items);
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), grid,
                                          dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
