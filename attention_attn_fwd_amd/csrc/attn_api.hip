@@ -84,9 +84,12 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Q == 0) return ATTN_OK;
   if (!supported_width(D) || !supported_width(Dv)) return ATTN_ERR_UNSUPPORTED;
-  // Offsets inside one (batch, head) slice are 32-bit in the kernels.
-  const int64_t lim = INT32_MAX;
-  if ((int64_t)Q * D > lim || (int64_t)Q * Dv > lim || (int64_t)K * D > lim || (int64_t)K * Dv > lim)
+  // Byte offsets inside one (batch, head) slice are 32-bit in the kernels, and
+  // the buffer loads read a padding channel as zero by giving it an offset
+  // of 2^31, past the end of any slice below that size.
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)Q * D * 2 >= lim || (int64_t)Q * Dv * 2 >= lim || (int64_t)K * D * 2 >= lim ||
+      (int64_t)K * Dv * 2 >= lim)
     return ATTN_ERR_UNSUPPORTED;
   const int group = Hq / Hkv;
   if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows) {
@@ -120,7 +123,10 @@ int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* 
   p.window = window > 0 ? window : 0;
   p.group = Hq / Hkv;
   p.q_sign = scale < 0.f ? 1 : 0;
-  p.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  // Kept strictly positive so a masked score (-inf) times it stays -inf; a
+  // zero scale becomes 1e-30, which changes no weight: every finite score
+  // times it rounds away against the reference max.
+  p.scale_log2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
   p.scale = scale;
   p.rows = p.group * Q;
 

@@ -86,15 +86,40 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
+// The same at a raw LDS byte address.
+__device__ __forceinline__ bf16x4 lds_read_tr16(uint32_t addr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(uintptr_t)(addr));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// 16-byte LDS read at a raw LDS byte address.
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  return *(const ATTN_LDS bf16x8*)(uintptr_t)(addr);
+}
+
+// max(a, b) and max(a, b, c) as single v_max_f32 / v_max3_f32.  Written as
+// asm because the compiler, to honour IEEE NaN quieting, otherwise
+// canonicalises each input (MFMA results, permlane results) with an extra
+// v_max first; the inputs here are finite or -inf.
+__device__ __forceinline__ float max2f(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // Butterfly over lanes l, l^16, l^32, l^48 using the gfx950 permlane swaps.
 __device__ __forceinline__ float xor16_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor16_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -7,23 +7,33 @@
 // Mapping on CDNA4:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
 //     owns 32 rows as two 16-column MFMA tiles, Q held in registers; two
-//     workgroups share a CU, so one's softmax overlaps the other's MFMAs;
+//     workgroups share a CU, so each SIMD runs one wave of each and the
+//     softmax of one overlaps the matrix products of the other;
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane holds 16 keys of
+//     one query column and the row max/sum is in-lane plus two permlane swaps;
+//     P^T stays in that register layout and feeds O^T = V^T P^T directly, V^T
+//     fragments read from row-major LDS through ds_read_b64_tr_b16;
 //   * K/V blocks of 64 keys go HBM -> LDS by direct buffer loads into a
 //     two-stage ring: block j+1 is in flight while block j is computed, one
 //     barrier per block; rows past K_b and channels past D read as zero from
 //     the buffer range check;
 //   * tiles are XOR-swizzled in LDS so the 16-byte K fragment reads and the
-//     transposed V reads are free of bank conflicts;
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane holds 16 keys of
-//     one query column and the row max/sum is in-lane plus two permlane swaps;
-//   * P^T stays in the S^T register layout and feeds O^T = V^T P^T directly;
-//     V^T fragments come from row-major LDS through ds_read_b64_tr_b16;
-//   * masks are evaluated only on blocks that straddle the causal diagonal, a
-//     window edge or the sequence end; blocks no row of a wave can see are
-//     skipped by that wave;
+//     transposed V reads are free of bank conflicts; the swizzle of a lane's
+//     fragment does not depend on the key tile, so every LDS address is one of
+//     a few per-lane registers plus an immediate (the loop is unrolled over
+//     the two ring stages so the stage offset is an immediate too);
+//   * the VALU work per block is kept to the softmax itself: wave-level
+//     control is scalar; masks are evaluated only on blocks that straddle the
+//     causal diagonal, a window edge or the sequence end, as the initial S^T
+//     accumulator (0 for a legal key, -inf otherwise); blocks no row of a wave
+//     can see are skipped by that wave; row maxima are v_max3 chains; and the
+//     running max moves only when a row's block max exceeds it by more than
+//     kLazyRescale;
 //   * tiles are ordered heaviest causal tile first, and the (batch, kv-head)
 //     groups are dealt to the 8 XCDs so the query heads sharing a kv-head run
 //     on one XCD and reuse its L2.
+#include <type_traits>
+
 #include "attn_internal.h"
 
 namespace attn {
@@ -39,9 +49,13 @@ struct PrefillShape {
   static constexpr int K_TILE = kPrefillBN * KROWB;
   static constexpr int V_TILE = kPrefillBN * VROWB;
   static constexpr int STAGE = K_TILE + V_TILE;
+  static constexpr int LDS = 2 * STAGE;
   static constexpr int K_LOADS = K_TILE / 4096;  // 16-byte loads per thread per block
   static constexpr int V_LOADS = V_TILE / 4096;
+  static constexpr int K_ROWS_PER_LOAD = 4096 / KROWB;  // tile rows one 4 KiB load round covers
+  static constexpr int V_ROWS_PER_LOAD = 4096 / VROWB;
   static_assert(K_TILE % 4096 == 0 && V_TILE % 4096 == 0, "load split");
+  static_assert(LDS <= 65536, "ds_read immediate offsets cover the ring");
 };
 
 // Block index -> (query tile, batch, head).  When the (batch, kv-head) groups
@@ -67,14 +81,18 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int n_qt, int* qt,
   }
 }
 
-template <int DP, int DVP>
+// EXACT: D == DP and Dv == DVP, so row strides are compile-time constants and
+// no channel is padding (the common case); otherwise padded channels read zero.
+template <int DP, int DVP, bool EXACT>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   using S = PrefillShape<DP, DVP>;
   constexpr int BN = kPrefillBN;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
+  const int D = EXACT ? DP : p.D;
+  const int Dv = EXACT ? DVP : p.Dv;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[S::LDS];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
   const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
@@ -94,16 +112,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
 
   const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Q * p.D;
-  const rsrc_t krs = slice_rsrc(static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D, (uint32_t)Kb * p.D * 2);
-  const rsrc_t vrs = slice_rsrc(static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv, (uint32_t)Kb * p.Dv * 2);
-  uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Q * p.Dv;
+  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Q * D;
+  const uint16_t* kslice = static_cast<const uint16_t*>(p.k) + kv_slice * p.K * D;
+  const uint16_t* vslice = static_cast<const uint16_t*>(p.v) + kv_slice * p.K * Dv;
+  uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Q * Dv;
   float* lg = p.lse + ((int64_t)b * p.Hq + h) * p.Q;
-  const int dch = p.D / 8, dvch = p.Dv / 8;
 
+  // Wave-level (scalar) row range and absolute positions.
   const int qw0 = q0 + wave * kPrefillRowsPerWave;
   const bool wave_has_rows = qw0 < p.Q;
   const int qw_last = min(qw0 + kPrefillRowsPerWave, p.Q) - 1;
+  const int pw_first = qw0 + delta, pw_last = qw_last + delta;
   const float c = p.scale_log2;
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
@@ -116,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
       const int col = 32 * s + 8 * g4;
-      uint4 u = (row < p.Q && col < p.D) ? load_u4(qg + (int64_t)row * p.D + col) : zero_u4();
+      uint4 u = (row < p.Q && col < D) ? load_u4(qg + (int64_t)row * D + col) : zero_u4();
       u.x ^= qx; u.y ^= qx; u.z ^= qx; u.w ^= qx;
       qf[t][s] = __builtin_bit_cast(bf16x8, u);
     }
@@ -128,135 +147,241 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) launder(qf[t][s]);
 
+  // Direct loads.  Load round i of wave w fills tile bytes [(4i + w) KiB,
+  // +1 KiB); lane l's 16 bytes land at position l of that KiB, so the lane
+  // fetches the global chunk the swizzle puts there.  A round covers a whole
+  // number of swizzle periods of rows, so the chunk a lane fetches is the same
+  // in every round and its global offset advances by a fixed step.
+  auto lane_off = [&](int rowb, int nch, bool is_v, int width) -> uint32_t {
+    const int off = wave * 1024 + 16 * lane;
+    const int row = off / rowb, pos = (off % rowb) >> 4;
+    const int ch = pos ^ (is_v ? ((2 * row) & (nch - 1)) : (row & (nch - 1)));
+    if (EXACT) return (uint32_t)(row * width + ch * 8) * 2;
+    return ch < width / 8 ? (uint32_t)(row * width + ch * 8) * 2 : kOutOfRange;
+  };
+  const uint32_t koff = lane_off(S::KROWB, S::KCH, false, D);
+  const uint32_t voff = lane_off(S::VROWB, S::VCH, true, Dv);
+  const uint32_t kstep = (uint32_t)(S::K_ROWS_PER_LOAD * D * 2);
+  const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv * 2);
+  const uint32_t lds0 = lds_offset(ring);
+  auto issue = [&](int jb, int stg) {
+    const int kb0 = jb * BN;
+    const uint32_t rows_left = (uint32_t)(Kb - kb0);
+    const rsrc_t rk = slice_rsrc(kslice + (int64_t)kb0 * D, rows_left * D * 2);
+    const rsrc_t rv = slice_rsrc(vslice + (int64_t)kb0 * Dv, rows_left * Dv * 2);
+    const uint32_t base = lds0 + stg * S::STAGE + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, base + i * 4096, koff + i * kstep);
+#pragma unroll
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, base + S::K_TILE + i * 4096, voff + i * vstep);
+  };
+
+  // Per-lane LDS read offsets (stage 0).  K fragment of k-step s, key tile i:
+  // row 16i + l16, chunk (4s + g4) ^ swz_k(row); swz_k(row) = l16 % KCH for
+  // every i.  V^T fragment of dv tile j: rows 32kk + 4*g4 + l16/4 (+16), chunk
+  // (2j + (l16 & 3)/2) ^ swz_v(row), half (l16 & 1); swz_v is the same for
+  // every kk and for the +16 row.
+  uint32_t ka[S::KS], va[S::JV];
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s)
+    ka[s] = lds0 + l16 * S::KROWB + ((((4 * s + g4) ^ swz_k<S::KCH>(l16))) << 4);
+  {
+    const int vrow = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int j = 0; j < S::JV; ++j)
+      va[j] = lds0 + S::K_TILE + vrow * S::VROWB + (((2 * j + ((l16 & 3) >> 1)) ^ swz_v<S::VCH>(vrow)) << 4) +
+              (l16 & 1) * 8;
+  }
+
+  // Whether any row of this wave has a legal key in block jb / every key of
+  // block jb is legal for every row of this wave (scalar).
+  auto wave_sees = [&](int jb) {
+    const int kb0 = jb * BN;
+    return wave_has_rows && kb0 <= pw_last && kb0 < Kb && !(W > 0 && kb0 + BN - 1 < pw_first - W + 1);
+  };
+  auto wave_full = [&](int jb) {
+    const int kb0 = jb * BN;
+    return (kb0 + BN - 1 <= pw_first) && (kb0 + BN <= Kb) && (W <= 0 || kb0 >= pw_last - W + 1);
+  };
+
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
   f32x4 acc[S::JV][2];
 #pragma unroll
   for (int j = 0; j < S::JV; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Direct loads of block jb into ring stage `stg`: each wave-wide load fills
-  // 1 KiB of the tile; lane l's 16 bytes land at position l of it, so the lane
-  // fetches the global chunk that the swizzle places there.
-  const uint32_t ring_base = lds_offset(ring);
-  auto issue = [&](int jb, int stg) {
-    const int kb0 = jb * BN;
-    const uint32_t kbase = ring_base + stg * S::STAGE;
+  // Initial S^T accumulator of a block that straddles the causal diagonal, a
+  // window edge or the sequence end: 0 for a legal key, -inf otherwise, so the
+  // products leave -inf at every illegal key.  Key kb0 + 4*g4 + x (x = 16i +
+  // r) is legal for query position pq iff lo <= x <= hi, with hi from
+  // causality and K_b and lo from the window: one unsigned compare against an
+  // immediate x per element.
+  auto mask_bias = [&](int kb0, f32x4 (&s)[4][2]) {
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) {
-      const int byte0 = (i * kPrefillWaves + wave) * 1024;
-      const int off = byte0 + 16 * lane;
-      const int row = off / S::KROWB, ch = ((off % S::KROWB) >> 4) ^ swz_k<S::KCH>(row);
-      const uint32_t vo = ch < dch ? ((uint32_t)(kb0 + row) * p.D + ch * 8) * 2 : kOutOfRange;
-      load_lds16(krs, kbase + __builtin_amdgcn_readfirstlane(byte0), vo);
-    }
-    const uint32_t vbase = kbase + S::K_TILE;
+    for (int t = 0; t < 2; ++t) {
+      const int rel = qw0 + 16 * t + l16 + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
+      const int hi = min(rel, Kb - kb0 - 4 * g4 - 1);
+      const int lo = W > 0 ? max(rel - W + 1, 0) : 0;
+      const uint32_t span = (uint32_t)(hi - lo);
+      const bool none = hi < lo;
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) {
-      const int byte0 = (i * kPrefillWaves + wave) * 1024;
-      const int off = byte0 + 16 * lane;
-      const int row = off / S::VROWB, ch = ((off % S::VROWB) >> 4) ^ swz_v<S::VCH>(row);
-      const uint32_t vo = ch < dvch ? ((uint32_t)(kb0 + row) * p.Dv + ch * 8) * 2 : kOutOfRange;
-      load_lds16(vrs, vbase + __builtin_amdgcn_readfirstlane(byte0), vo);
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool legal = !none & ((uint32_t)(16 * i + r - lo) <= span);
+          s[i][t][r] = legal ? 0.f : -INFINITY;
+        }
+      }
     }
   };
 
-  if (jb0 < jb1) issue(jb0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
+  // Block row max in log2 units (-inf: no legal key in the block; the scale
+  // factor c is positive, so -inf * c stays -inf).
+  auto block_max = [&](const f32x4 (&s)[4][2], float (&mb)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
+      mx = max3f(mx, s[0][t][3], s[1][t][0]);
+      mx = max3f(mx, s[1][t][1], s[1][t][2]);
+      mx = max3f(mx, s[1][t][3], s[2][t][0]);
+      mx = max3f(mx, s[2][t][1], s[2][t][2]);
+      mx = max3f(mx, s[2][t][3], s[3][t][0]);
+      mx = max3f(mx, s[3][t][1], s[3][t][2]);
+      mx = max2f(mx, s[3][t][3]);
+      mb[t] = group4_max(mx) * c;
+    }
+  };
 
-  for (int jb = jb0; jb < jb1; ++jb) {
-    const int stg = (jb - jb0) & 1;
-    if (jb + 1 < jb1) issue(jb + 1, stg ^ 1);
-    const unsigned char* kst = ring + stg * S::STAGE;
-    const unsigned char* vst = kst + S::K_TILE;
-    const int kb0 = jb * BN;
-    const int pw_first = qw0 + delta, pw_last = qw_last + delta;
-    const bool skip = !wave_has_rows || kb0 > pw_last || kb0 >= Kb || (W > 0 && kb0 + BN - 1 < pw_first - W + 1);
-    if (!skip) {
-      const bool full = (kb0 + BN - 1 <= pw_first) && (kb0 + BN <= Kb) && (W <= 0 || kb0 >= pw_last - W + 1);
-      f32x4 sacc[4][2];
+  // Online softmax update from the block max: moves the lazy reference when
+  // some lane of the wave needs it (rescaling row sums and accumulators), then
+  // turns the scores into bf16 weights in pf and adds them to the row sums.
+  // A row whose reference is still -inf has only -inf scores here (a legal
+  // key would have moved it), so its offset is taken as 0 to give 2^-inf = 0.
+  auto softmax = [&](f32x4 (&s)[4][2], const float (&mb)[2], bf16x8 (&pf)[2][2]) {
+    const bool need = (mb[0] > m_run[0] + kLazyRescale) || (mb[1] > m_run[1] + kLazyRescale);
+    if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[i][0] = sacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 2; ++t) {
+        const float mnew = fmaxf(m_run[t], mb[t]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
+        m_run[t] = mnew;
+        l_run[t] *= alpha;
 #pragma unroll
-      for (int s = 0; s < S::KS; ++s) {
+        for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * i + l16;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              kst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
-          sacc[i][0] = mfma16x16x32(a, qf[0][s], sacc[i][0]);
-          sacc[i][1] = mfma16x16x32(a, qf[1][s], sacc[i][1]);
+    for (int t = 0; t < 2; ++t) {
+      const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = fast_exp2(fmaf(s[i][t][r], c, mneg));
+          s[i][t][r] = e;
+          rs += e;
         }
       }
-      if (!full) {
+      l_run[t] += rs;
+      pf[t][0] = pack_bf16x8(s[0][t], s[1][t]);
+      pf[t][1] = pack_bf16x8(s[2][t], s[3][t]);
+    }
+  };
+
+  // One KV block in ring stage STG (a compile-time constant, so every LDS
+  // address below is a per-lane register plus an immediate).  Only the
+  // initial accumulator of S^T differs between blocks whose keys are all
+  // legal for every row of the wave (FULL: zero, an inline constant) and the
+  // rest (mask_bias).
+  auto body = [&](int jb, auto stg_tag, bool full) {
+    constexpr int STG = decltype(stg_tag)::value;
+    constexpr uint32_t SOFF = STG * S::STAGE;
+    {
+      const int kb0 = jb * BN;
+      f32x4 s[4][2];
+      // S^T = K Q^T.  The K fragments of k-step st + 1 are read while the
+      // MFMAs of k-step st run; the fences keep the compiler from hoisting
+      // every read of the block (64 registers) ahead of the products.
+      auto qk = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        bf16x8 ak[2][4];
+        if constexpr (!FULL) mask_bias(kb0, s);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int pq = qw0 + 16 * t + l16 + delta;
+        for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(ka[0] + SOFF + 16 * i * S::KROWB);
+#pragma unroll
+        for (int st = 0; st < S::KS; ++st) {
+          if (st + 1 < S::KS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(ka[st + 1] + SOFF + 16 * i * S::KROWB);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = kb0 + 16 * i + 4 * g4 + r;
-              const bool legal = key <= pq && key < Kb && (W <= 0 || key > pq - W);
-              if (!legal) sacc[i][t][r] = -INFINITY;
+            for (int t = 0; t < 2; ++t) {
+              const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
+              s[i][t] = mfma16x16x32(ak[st & 1][i], qf[t][st], c0);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      };
+      if (full) qk(std::true_type{});
+      else qk(std::false_type{});
+      // V^T fragment of (kk, j): rows 32kk + 4*g4 + l16/4 and 16 below.
+      auto read_v = [&](int kk, int j) {
+        const uint32_t lo = va[j] + SOFF + 32 * kk * S::VROWB;
+        return concat_bf16x4(lds_read_tr16(lo), lds_read_tr16(lo + 16 * S::VROWB));
+      };
+      // The first two V fragments are in flight during the softmax.
+      bf16x8 av[2][2];
+      av[0][0] = read_v(0, 0);
+      av[0][1] = read_v(0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      float mb[2];
+      block_max(s, mb);
       bf16x8 pf[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float mx = sacc[0][t][0];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[i][t][r]);
-        mx = group4_max(mx);
-        const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
-        float alpha;
-        if (softmax_rebase(m_run[t], mb, alpha)) {
-          l_run[t] *= alpha;
-#pragma unroll
-          for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
-        }
-        const float mref = m_run[t];
-        float rs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sv = sacc[i][t][r];
-            float e = fast_exp2(fmaf(sv, c, -mref));
-            if (!full) e = (sv == -INFINITY) ? 0.f : e;
-            sacc[i][t][r] = e;
-            rs += e;
-          }
-        }
-        l_run[t] += rs;
-        pf[t][0] = pack_bf16x8(sacc[0][t], sacc[1][t]);
-        pf[t][1] = pack_bf16x8(sacc[2][t], sacc[3][t]);
-      }
-      // O^T += V^T P^T over two 32-key halves.  The contraction index e of the
-      // B operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 + e - 4,
+      softmax(s, mb, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T over two 32-key halves, two dv tiles per step with the
+      // next step's fragments in flight.  The contraction index e of the B
+      // operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 + e - 4,
       // the S^T register layout; the V^T fragment is read in the same order.
+      constexpr int NP = 2 * (S::JV / 2);  // steps of two dv tiles over both halves
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int row = 32 * kk + 4 * g4 + (l16 >> 2);
-#pragma unroll
-        for (int j = 0; j < S::JV; ++j) {
-          const int ch = 2 * j + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
-          const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
-          const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
-          const bf16x8 va = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
-                                          lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
-          acc[j][0] = mfma16x16x32(va, pf[0][kk], acc[j][0]);
-          acc[j][1] = mfma16x16x32(va, pf[1][kk], acc[j][1]);
+      for (int n = 0; n < NP; ++n) {
+        const int kk = n / (S::JV / 2), j = 2 * (n % (S::JV / 2));
+        if (n + 1 < NP) {
+          const int kk1 = (n + 1) / (S::JV / 2), j1 = 2 * ((n + 1) % (S::JV / 2));
+          av[(n + 1) & 1][0] = read_v(kk1, j1);
+          av[(n + 1) & 1][1] = read_v(kk1, j1 + 1);
         }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[j + u][0] = mfma16x16x32(av[n & 1][u], pf[0][kk], acc[j + u][0]);
+          acc[j + u][1] = mfma16x16x32(av[n & 1][u], pf[1][kk], acc[j + u][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // Block jb+1 has landed for every wave, and every wave is done with stage stg.
+  };
+  auto block = [&](int jb, auto stg_tag) {
+    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1);
+    if (wave_sees(jb)) body(jb, stg_tag, wave_full(jb));
+    // Block jb + 1 has landed for every wave, and every wave is done with
+    // the stage of block jb, which the next block's loads overwrite.
     wait_vmcnt<0>();
     __syncthreads();
+  };
+
+  if (jb0 < jb1) {
+    issue(jb0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  for (int jb = jb0; jb < jb1; jb += 2) {
+    block(jb, std::integral_constant<int, 0>{});
+    if (jb + 1 < jb1) block(jb + 1, std::integral_constant<int, 1>{});
   }
 
   if (!wave_has_rows) return;
@@ -269,13 +394,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < S::JV; ++j) {
         const int dv = 16 * j + 4 * g4;
-        if (dv < p.Dv) {
+        if (dv < Dv) {
           bf16x4 ov;
           ov[0] = (__bf16)(acc[j][t][0] * inv);
           ov[1] = (__bf16)(acc[j][t][1] * inv);
           ov[2] = (__bf16)(acc[j][t][2] * inv);
           ov[3] = (__bf16)(acc[j][t][3] * inv);
-          *reinterpret_cast<bf16x4*>(og + (int64_t)row * p.Dv + dv) = ov;
+          *reinterpret_cast<bf16x4*>(og + (int64_t)row * Dv + dv) = ov;
         }
       }
       if (g4 == 0) lg[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
@@ -289,8 +414,9 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)n_qt * p.Hq * p.B));
   Params arg = p;
   void* args[] = {&arg};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP>), grid, dim3(256), args, 0,
-                         stream);
+  const void* fn = (p.D == DP && p.Dv == DVP) ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true>)
+                                              : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false>);
+  return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream) {

@@ -66,7 +66,9 @@ enum attn_status {
  *   ATTN_ERR_INVALID_ARG  a negative size; Hq > 0 with Hkv == 0 or
  *                         Hq % Hkv != 0; a non-finite scale; q/o/lse NULL
  *                         while B*Hq*Q > 0; k/v NULL while B*Hkv*K > 0;
- *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 128];
+ *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 128]; or one
+ *                         (batch, head) slice of 2 GiB or more in bf16
+ *                         (Q*D, Q*Dv, K*D or K*Dv >= 2^30 elements);
  *   ATTN_ERR_OOM, ATTN_ERR_HIP as above;
  *   ATTN_OK               also when B*Hq*Q == 0 (nothing launched).
  * K == 0, or every K_b == 0, writes O = 0 and LSE = -inf for all rows.

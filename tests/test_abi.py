@@ -45,6 +45,9 @@ BAD = [
     (1, 4, 2, 8, 8, 64, 7, 1.0, af.ATTN_ERR_UNSUPPORTED),
     (1, 4, 2, 8, 8, 256, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 128
     (1, 4, 2, 8, 8, 0, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),
+    (1, 4, 2, 8, 1 << 23, 128, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*D = 2^30: a 2 GiB slice
+    (1, 4, 2, 8, 1 << 23, 64, 128, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*Dv = 2^30
+    (1, 4, 2, 1 << 23, 8, 128, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),  # Q*D = 2^30
 ]
 
 
@@ -70,6 +73,14 @@ def test_empty_problem_is_ok_without_launch(fn):
     for (B, Hq, Q) in [(0, 4, 8), (1, 0, 8), (2, 4, 0)]:
         Hkv = 2 if Hq else 0
         assert fn(None, None, None, None, None, B, Hq, Hkv, Q, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_OK
+
+
+def test_slice_size_limit_boundary():
+    # One row short of a 2 GiB (batch, head) slice is accepted by the plan.
+    assert af.attn_fwd_plan(1, 4, 2, 8, (1 << 23) - 1, 128, 128)["path"] == af.PATH_PREFILL
+    with pytest.raises(af.AttnError) as e:
+        af.attn_fwd_plan(1, 4, 2, 8, 1 << 23, 128, 128)
+    assert e.value.status == af.ATTN_ERR_UNSUPPORTED
 
 
 def test_plan_selects_paths():
