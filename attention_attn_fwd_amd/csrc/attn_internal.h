@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 // Workgroup geometry of the bf16 prefill kernel: 4 waves of 64 lanes, each
@@ -151,6 +153,16 @@ __device__ __forceinline__ bool softmax_rebase(float& m_run, float mb, float& al
   alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run - mnew);
   m_run = mnew;
   return true;
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1, so the body can
+// branch on i at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 // Pack eight floats into bf16 (round to nearest even).
