@@ -10,11 +10,12 @@
 
 namespace attn {
 
-// Workgroup geometry of the bf16 prefill kernel: 4 waves of 64 lanes, each
-// wave owning 32 query rows (two 16-column MFMA tiles), 64 keys per KV block.
+// Workgroup geometry of the bf16 prefill kernel: kPrefillWaves waves of 64
+// lanes, each wave owning 32 query rows (two 16-column MFMA tiles), 64 keys
+// per KV block.
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRowsPerWave = 32;
-constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // 128 query rows
+constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // query rows per workgroup
 constexpr int kPrefillBN = 64;                                   // keys per block
 
 // Split-KV decode: single-wave workgroups streaming 32-key sub-blocks; chunks

@@ -7,33 +7,28 @@
 // Mapping on CDNA4:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
 //     owns 32 rows as two 16-column MFMA tiles, Q held in registers; two
-//     workgroups share a CU, so each SIMD runs one wave of each;
+//     workgroups share a CU, so each SIMD runs one wave of each and the
+//     softmax of one overlaps the matrix products of the other;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane holds 16 keys of
 //     one query column and the row max/sum is in-lane plus two permlane swaps;
 //     P^T stays in that register layout and feeds O^T = V^T P^T directly, V^T
 //     fragments read from row-major LDS through ds_read_b64_tr_b16;
-//   * software pipeline over KV blocks of 64 keys: while a wave runs the
-//     softmax of block j on the VALU, the MFMA unit computes S^T of block j+1
-//     (the FlyDSL FMHA post describes the same overlap of one tile's softmax
-//     with another tile's matrix products), then P.V of block j; so K runs
-//     one block ahead of V, in a three-stage LDS ring against V's two stages
-//     (80 KiB at D = Dv = 128, two workgroups per CU);
-//   * K/V blocks go HBM -> LDS by direct buffer loads issued a step ahead, one
+//   * K/V blocks of 64 keys go HBM -> LDS by direct buffer loads into a
+//     two-stage ring: block j+1 is in flight while block j is computed, one
 //     barrier per block; rows past K_b and channels past D read as zero from
 //     the buffer range check;
 //   * tiles are XOR-swizzled in LDS so the 16-byte K fragment reads and the
-//     transposed V reads are free of bank conflicts; a lane's fragment
-//     addresses are one register XOR a k-step or dv-tile constant, plus an
-//     immediate for the key tile and the V stage (the loop is unrolled over
-//     the two V stages);
+//     transposed V reads are free of bank conflicts; the swizzle of a lane's
+//     fragment does not depend on the key tile, so every LDS address is one of
+//     a few per-lane registers plus an immediate (the loop is unrolled over
+//     the two ring stages so the stage offset is an immediate too);
 //   * the VALU work per block is kept to the softmax itself: wave-level
 //     control is scalar; masks are evaluated only on blocks that straddle the
 //     causal diagonal, a window edge or the sequence end, as the initial S^T
 //     accumulator (0 for a legal key, -inf otherwise); blocks no row of a wave
 //     can see are skipped by that wave; row maxima are v_max3 chains; and the
 //     running max moves only when a row's block max exceeds it by more than
-//     kLazyRescale (the accumulators are rescaled in a branch after the
-//     interleaved section);
+//     kLazyRescale;
 //   * tiles are ordered heaviest causal tile first within a (batch, kv-head)
 //     group, and the groups are dealt to the 8 XCDs so an XCD streams one
 //     group's K/V through its L2 at a time.
@@ -53,14 +48,14 @@ struct PrefillShape {
   static constexpr int VROWB = DVP * 2;
   static constexpr int K_TILE = kPrefillBN * KROWB;
   static constexpr int V_TILE = kPrefillBN * VROWB;
-  static constexpr int K_STAGES = 3;        // K runs one block ahead of V
-  static constexpr int V_BASE = K_STAGES * K_TILE;
-  static constexpr int LDS = V_BASE + 2 * V_TILE;
+  static constexpr int STAGE = K_TILE + V_TILE;
+  static constexpr int LDS = 2 * STAGE;
   static constexpr int K_LOADS = K_TILE / 4096;  // 16-byte loads per thread per block
   static constexpr int V_LOADS = V_TILE / 4096;
   static constexpr int K_ROWS_PER_LOAD = 4096 / KROWB;  // tile rows one 4 KiB load round covers
   static constexpr int V_ROWS_PER_LOAD = 4096 / VROWB;
   static_assert(K_TILE % 4096 == 0 && V_TILE % 4096 == 0, "load split");
+  static_assert(LDS <= 65536, "ds_read immediate offsets cover the ring");
 };
 
 // Block index -> (query tile, batch, head).  When the (batch, kv-head) groups
@@ -172,27 +167,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const uint32_t kstep = (uint32_t)(S::K_ROWS_PER_LOAD * D * 2);
   const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv * 2);
   const uint32_t lds0 = lds_offset(ring);
-  // K of block jb lives in K stage (jb - jb0) % 3, V in V stage (jb - jb0) % 2.
-  auto kstage_off = [&](int jb) -> uint32_t { return (uint32_t)((jb - jb0) % S::K_STAGES) * S::K_TILE; };
-  // The per-round offsets are formed at each issue (the base is laundered so
-  // the compiler does not keep all of them live across the loop).
-  auto issue_k = [&](int jb) {
+  auto issue = [&](int jb, int stg) {
     const int kb0 = jb * BN;
-    const rsrc_t rk = slice_rsrc(kslice + (int64_t)kb0 * D, (uint32_t)(Kb - kb0) * D * 2);
-    const uint32_t base = lds0 + kstage_off(jb) + wave * 1024;
-    uint32_t o = koff;
-    launder(o);
+    const uint32_t rows_left = (uint32_t)(Kb - kb0);
+    const rsrc_t rk = slice_rsrc(kslice + (int64_t)kb0 * D, rows_left * D * 2);
+    const rsrc_t rv = slice_rsrc(vslice + (int64_t)kb0 * Dv, rows_left * Dv * 2);
+    const uint32_t base = lds0 + stg * S::STAGE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, base + i * 4096, o + i * kstep);
-  };
-  auto issue_v = [&](int jb, int vst) {
-    const int kb0 = jb * BN;
-    const rsrc_t rv = slice_rsrc(vslice + (int64_t)kb0 * Dv, (uint32_t)(Kb - kb0) * Dv * 2);
-    const uint32_t base = lds0 + S::V_BASE + vst * S::V_TILE + wave * 1024;
-    uint32_t o = voff;
-    launder(o);
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, base + i * 4096, koff + i * kstep);
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, base + i * 4096, o + i * vstep);
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, base + S::K_TILE + i * 4096, voff + i * vstep);
   };
 
   // Per-lane LDS read offsets (stage 0).  K fragment of k-step s, key tile i:
@@ -200,17 +184,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // every i.  V^T fragment of dv tile j: rows 32kk + 4*g4 + l16/4 (+16), chunk
   // (2j + (l16 & 3)/2) ^ swz_v(row), half (l16 & 1); swz_v is the same for
   // every kk and for the +16 row.
-  // With the K row stride a multiple of 128 bytes the chunk bits of the
-  // offset start at bit 4, so the address for k-step s is ka0 ^ (s << 6)
-  // ((4s + g4) ^ swz = 4s ^ (g4 ^ swz)): one register instead of KS.
-  static_assert(S::KROWB % 128 == 0 && S::K_TILE % 256 == 0, "K address bits");
-  const uint32_t ka0 = lds0 + l16 * S::KROWB + (((g4 ^ swz_k<S::KCH>(l16))) << 4);
-  // Likewise the V^T fragment of dv tile j is at va0 ^ (j << 5): swz_v is
-  // even, so (2j + b) ^ swz = 2j ^ (b + swz) and the chunk bits start at 4.
-  static_assert(S::VROWB % 128 == 0 && S::V_BASE % 256 == 0, "V address bits");
-  const int vrow = 4 * g4 + (l16 >> 2);
-  const uint32_t va0 =
-      lds0 + S::V_BASE + vrow * S::VROWB + ((((l16 & 3) >> 1) ^ swz_v<S::VCH>(vrow)) << 4) + (l16 & 1) * 8;
+  uint32_t ka[S::KS], va[S::JV];
+#pragma unroll
+  for (int s = 0; s < S::KS; ++s)
+    ka[s] = lds0 + l16 * S::KROWB + ((((4 * s + g4) ^ swz_k<S::KCH>(l16))) << 4);
+  {
+    const int vrow = 4 * g4 + (l16 >> 2);
+#pragma unroll
+    for (int j = 0; j < S::JV; ++j)
+      va[j] = lds0 + S::K_TILE + vrow * S::VROWB + (((2 * j + ((l16 & 3) >> 1)) ^ swz_v<S::VCH>(vrow)) << 4) +
+              (l16 & 1) * 8;
+  }
 
   // Whether any row of this wave has a legal key in block jb / every key of
   // block jb is legal for every row of this wave (scalar).
@@ -254,21 +238,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     }
   };
 
-  // Online softmax of one block's scores, in parts that can be spread over
-  // the MFMAs of the next block's K Q^T.  sm_max: block row max (v_max3 chain
-  // + two permlane swaps; -inf: no legal key, and c > 0 keeps -inf * c at
-  // -inf), lazy reference update (it moves only when some lane of the wave
-  // needs it; the wave-uniform result tells the caller to multiply its
-  // accumulators by alpha).  sm_exp(t, ih): weights 2^(s*c - m) of key tiles
-  // 2ih, 2ih+1 of query tile t, rounded to bf16 in pf, summed into the row
-  // sum.  A row whose reference is still -inf has only -inf scores (a legal
-  // key would have moved it), so its offset is taken as 0 to give 2^-inf = 0.
-  struct SoftmaxState {
-    float alpha[2], mneg[2], rs[2];
-    bool rebase;
-  };
-  auto sm_max = [&](const f32x4 (&s)[4][2], SoftmaxState& st) {
-    float mb[2];
+  // Block row max in log2 units (-inf: no legal key in the block; the scale
+  // factor c is positive, so -inf * c stays -inf).
+  auto block_max = [&](const f32x4 (&s)[4][2], float (&mb)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
@@ -281,176 +253,138 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       mx = max2f(mx, s[3][t][3]);
       mb[t] = group4_max(mx) * c;
     }
-    const bool need = (mb[0] > m_run[0] + kLazyRescale) || (mb[1] > m_run[1] + kLazyRescale);
-    st.rebase = __builtin_amdgcn_ballot_w64(need) != 0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const float mnew = st.rebase ? fmaxf(m_run[t], mb[t]) : m_run[t];
-      st.alpha[t] = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
-      st.mneg[t] = mnew == -INFINITY ? 0.f : -mnew;
-      m_run[t] = mnew;
-    }
-  };
-  auto sm_exp = [&](int t, int ih, f32x4 (&s)[4][2], bf16x8 (&pf)[2][2], SoftmaxState& st) {
-#pragma unroll
-    for (int i = 2 * ih; i < 2 * ih + 2; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = fast_exp2(fmaf(s[i][t][r], c, st.mneg[t]));
-        s[i][t][r] = e;
-        st.rs[t] = (ih == 0 && i == 0 && r == 0) ? e : st.rs[t] + e;
-      }
-    }
-    pf[t][ih] = pack_bf16x8(s[2 * ih][t], s[2 * ih + 1][t]);
-  };
-  auto sm_fin = [&](SoftmaxState& st) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) l_run[t] = fmaf(l_run[t], st.alpha[t], st.rs[t]);
   };
 
-  // S^T = K Q^T of block jb into s (FULL: every key legal for every row, the
-  // initial accumulator is the inline constant 0; otherwise mask_bias), with
-  // the K fragments of k-step st + 1 read while the MFMAs of k-step st run.
-  // When `cur` is given, the softmax of the previous block (scores in cur) is
-  // spread over the k-steps: its row max with k-step 0, its four weight
-  // groups over the others, for the compiler to interleave with the MFMAs.
-  auto qk = [&](int jb, auto full_tag, f32x4 (&s)[4][2], auto with_softmax, f32x4 (&cur)[4][2],
-                bf16x8 (&pf)[2][2], SoftmaxState& sm) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    constexpr bool SM = decltype(with_softmax)::value;
-    const uint32_t kbase = ka0 + kstage_off(jb);
-    auto kaddr = [&](int st) { return kbase ^ (uint32_t)(st << 6); };
-    if constexpr (!FULL) mask_bias(jb * BN, s);
-    bf16x8 ak[2][4];
+  // Online softmax update from the block max: moves the lazy reference when
+  // some lane of the wave needs it (rescaling row sums and accumulators), then
+  // turns the scores into bf16 weights in pf and adds them to the row sums.
+  // A row whose reference is still -inf has only -inf scores here (a legal
+  // key would have moved it), so its offset is taken as 0 to give 2^-inf = 0.
+  auto softmax = [&](f32x4 (&s)[4][2], const float (&mb)[2], bf16x8 (&pf)[2][2]) {
+    const bool need = (mb[0] > m_run[0] + kLazyRescale) || (mb[1] > m_run[1] + kLazyRescale);
+    if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(kaddr(0) + 16 * i * S::KROWB);
-    static_for<S::KS>([&](auto st_tag) {
-      constexpr int st = decltype(st_tag)::value;
-      if constexpr (st + 1 < S::KS) {
+      for (int t = 0; t < 2; ++t) {
+        const float mnew = fmaxf(m_run[t], mb[t]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
+        m_run[t] = mnew;
+        l_run[t] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(kaddr(st + 1) + 16 * i * S::KROWB);
+        for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
       }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
+      float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
-          s[i][t] = mfma16x16x32(ak[st & 1][i], qf[t][st], c0);
+        for (int r = 0; r < 4; ++r) {
+          const float e = fast_exp2(fmaf(s[i][t][r], c, mneg));
+          s[i][t][r] = e;
+          rs += e;
         }
       }
-      if constexpr (SM) {
-        if constexpr (st == 0) sm_max(cur, sm);
-        static_for<4>([&](auto e_tag) {
-          constexpr int e = decltype(e_tag)::value;
-          if constexpr (S::KS > 1 && 1 + e * (S::KS - 1) / 4 == st) sm_exp(e >> 1, e & 1, cur, pf, sm);
-        });
-        if constexpr (st == S::KS - 1) sm_fin(sm);
-      }
-    });
+      l_run[t] += rs;
+      pf[t][0] = pack_bf16x8(s[0][t], s[1][t]);
+      pf[t][1] = pack_bf16x8(s[2][t], s[3][t]);
+    }
   };
 
-  // O^T += V^T P^T of block jb from V stage VST, two dv tiles per step with
-  // the next step's fragments in flight.  The contraction index e of the B
-  // operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 + e - 4,
-  // the S^T register layout; the V^T fragment is read in the same order.
-  auto pv = [&](auto vst_tag, const bf16x8 (&pf)[2][2]) {
-    constexpr uint32_t VOFF = decltype(vst_tag)::value * S::V_TILE;
-    auto read_v = [&](int kk, int j) {
-      const uint32_t lo = (va0 ^ (uint32_t)(j << 5)) + VOFF + 32 * kk * S::VROWB;
-      return concat_bf16x4(lds_read_tr16(lo), lds_read_tr16(lo + 16 * S::VROWB));
-    };
-    constexpr int NP = S::JV;  // steps of two dv tiles over both 32-key halves
-    bf16x8 av[2][2];
-    av[0][0] = read_v(0, 0);
-    av[0][1] = read_v(0, 1);
+  // One KV block in ring stage STG (a compile-time constant, so every LDS
+  // address below is a per-lane register plus an immediate).  Only the
+  // initial accumulator of S^T differs between blocks whose keys are all
+  // legal for every row of the wave (FULL: zero, an inline constant) and the
+  // rest (mask_bias).
+  auto body = [&](int jb, auto stg_tag, bool full) {
+    constexpr int STG = decltype(stg_tag)::value;
+    constexpr uint32_t SOFF = STG * S::STAGE;
+    {
+      const int kb0 = jb * BN;
+      f32x4 s[4][2];
+      // S^T = K Q^T.  The K fragments of k-step st + 1 are read while the
+      // MFMAs of k-step st run; the fences keep the compiler from hoisting
+      // every read of the block (64 registers) ahead of the products.
+      auto qk = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        bf16x8 ak[2][4];
+        if constexpr (!FULL) mask_bias(kb0, s);
 #pragma unroll
-    for (int n = 0; n < NP; ++n) {
-      const int kk = n / (S::JV / 2), j = 2 * (n % (S::JV / 2));
-      if (n + 1 < NP) {
-        const int kk1 = (n + 1) / (S::JV / 2), j1 = 2 * ((n + 1) % (S::JV / 2));
-        av[(n + 1) & 1][0] = read_v(kk1, j1);
-        av[(n + 1) & 1][1] = read_v(kk1, j1 + 1);
-      }
+        for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(ka[0] + SOFF + 16 * i * S::KROWB);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        acc[j + u][0] = mfma16x16x32(av[n & 1][u], pf[0][kk], acc[j + u][0]);
-        acc[j + u][1] = mfma16x16x32(av[n & 1][u], pf[1][kk], acc[j + u][1]);
-      }
+        for (int st = 0; st < S::KS; ++st) {
+          if (st + 1 < S::KS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(ka[st + 1] + SOFF + 16 * i * S::KROWB);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
+              s[i][t] = mfma16x16x32(ak[st & 1][i], qf[t][st], c0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      if (full) qk(std::true_type{});
+      else qk(std::false_type{});
+      // V^T fragment of (kk, j): rows 32kk + 4*g4 + l16/4 and 16 below.
+      auto read_v = [&](int kk, int j) {
+        const uint32_t lo = va[j] + SOFF + 32 * kk * S::VROWB;
+        return concat_bf16x4(lds_read_tr16(lo), lds_read_tr16(lo + 16 * S::VROWB));
+      };
+      // The first two V fragments are in flight during the softmax.
+      bf16x8 av[2][2];
+      av[0][0] = read_v(0, 0);
+      av[0][1] = read_v(0, 1);
       __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  auto kill = [](f32x4 (&x)[4][2]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i][0] = x[i][1] = __builtin_nondeterministic_value(x[i][0]);
-  };
-
-  // One pipeline step: the softmax of block jb (scores in cur) runs while the
-  // MFMA unit computes S^T of block jb + 1 (into nxt); then P.V of block jb.
-  // The loads issued here (K of jb + 2, V of jb + 1) have the whole step to
-  // land.
-  auto step = [&](int jb, auto vst_tag, f32x4 (&cur)[4][2], f32x4 (&nxt)[4][2]) {
-    constexpr int VST = decltype(vst_tag)::value;
-    if (jb + 2 < jb1) issue_k(jb + 2);
-    if (jb + 1 < jb1) issue_v(jb + 1, VST ^ 1);
-    const bool now = wave_sees(jb);
-    const bool next = jb + 1 < jb1 && wave_sees(jb + 1);
-    // A step reads cur only if the wave sees block jb, and the next step reads
-    // nxt only if it sees block jb + 1; telling the compiler so frees the
-    // registers of a score buffer that holds nothing of use.
-    if (!next) kill(nxt);
-    bf16x8 pf[2][2];
-    SoftmaxState sm;
-    if (now) {
-      if (next) {
-        if (wave_full(jb + 1)) qk(jb + 1, std::true_type{}, nxt, std::true_type{}, cur, pf, sm);
-        else qk(jb + 1, std::false_type{}, nxt, std::true_type{}, cur, pf, sm);
-      } else {
-        sm_max(cur, sm);
-        sm_exp(0, 0, cur, pf, sm);
-        sm_exp(0, 1, cur, pf, sm);
-        sm_exp(1, 0, cur, pf, sm);
-        sm_exp(1, 1, cur, pf, sm);
-        sm_fin(sm);
-      }
-      if (sm.rebase) {
-#pragma unroll
-        for (int j = 0; j < S::JV; ++j) {
-          acc[j][0] *= sm.alpha[0];
-          acc[j][1] *= sm.alpha[1];
-        }
-      }
-      pv(vst_tag, pf);
-    } else if (next) {
-      if (wave_full(jb + 1)) qk(jb + 1, std::true_type{}, nxt, std::false_type{}, cur, pf, sm);
-      else qk(jb + 1, std::false_type{}, nxt, std::false_type{}, cur, pf, sm);
-    }
-    kill(cur);
-    // K of jb + 2 and V of jb + 1 have landed for every wave, and every wave
-    // is done with the stages they overwrite next step.
-    wait_vmcnt<0>();
-    __syncthreads();
-  };
-
-  f32x4 s0[4][2], s1[4][2];
-  if (jb0 < jb1) {
-    issue_k(jb0);
-    issue_v(jb0, 0);
-    if (jb0 + 1 < jb1) issue_k(jb0 + 1);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (wave_sees(jb0)) {
+      float mb[2];
+      block_max(s, mb);
       bf16x8 pf[2][2];
-      SoftmaxState sm;
-      if (wave_full(jb0)) qk(jb0, std::true_type{}, s0, std::false_type{}, s1, pf, sm);
-      else qk(jb0, std::false_type{}, s0, std::false_type{}, s1, pf, sm);
+      softmax(s, mb, pf);
+      __builtin_amdgcn_sched_barrier(0);
+      // O^T += V^T P^T over two 32-key halves, two dv tiles per step with the
+      // next step's fragments in flight.  The contraction index e of the B
+      // operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 + e - 4,
+      // the S^T register layout; the V^T fragment is read in the same order.
+      constexpr int NP = 2 * (S::JV / 2);  // steps of two dv tiles over both halves
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        const int kk = n / (S::JV / 2), j = 2 * (n % (S::JV / 2));
+        if (n + 1 < NP) {
+          const int kk1 = (n + 1) / (S::JV / 2), j1 = 2 * ((n + 1) % (S::JV / 2));
+          av[(n + 1) & 1][0] = read_v(kk1, j1);
+          av[(n + 1) & 1][1] = read_v(kk1, j1 + 1);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[j + u][0] = mfma16x16x32(av[n & 1][u], pf[0][kk], acc[j + u][0]);
+          acc[j + u][1] = mfma16x16x32(av[n & 1][u], pf[1][kk], acc[j + u][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+  };
+  auto block = [&](int jb, auto stg_tag) {
+    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1);
+    if (wave_sees(jb)) body(jb, stg_tag, wave_full(jb));
+    // Block jb + 1 has landed for every wave, and every wave is done with
+    // the stage of block jb, which the next block's loads overwrite.
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  if (jb0 < jb1) {
+    issue(jb0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
   }
-  // Unrolled by two: the score buffers swap roles and the V stage is a
-  // compile-time constant in each half.
   for (int jb = jb0; jb < jb1; jb += 2) {
-    step(jb, std::integral_constant<int, 0>{}, s0, s1);
-    if (jb + 1 < jb1) step(jb + 1, std::integral_constant<int, 1>{}, s1, s0);
+    block(jb, std::integral_constant<int, 0>{});
+    if (jb + 1 < jb1) block(jb + 1, std::integral_constant<int, 1>{});
   }
 
   if (!wave_has_rows) return;
