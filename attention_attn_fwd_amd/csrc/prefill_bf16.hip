@@ -26,9 +26,9 @@
 //     control is scalar; masks are evaluated only on blocks that straddle the
 //     causal diagonal, a window edge or the sequence end, as the initial S^T
 //     accumulator (0 for a legal key, -inf otherwise); blocks no row of a wave
-//     can see are skipped by that wave; row maxima are v_max3 chains; and the
-//     running max moves only when a row's block max exceeds it by more than
-//     kLazyRescale;
+//     can see are skipped by that wave; and the running max is lazy: weights
+//     are formed against the current reference and the block max is computed
+//     only when a partial row sum shows a weight may exceed 2^kLazyRescale;
 //   * tiles are ordered heaviest causal tile first within a (batch, kv-head)
 //     group, and the groups are dealt to the 8 XCDs so an XCD streams one
 //     group's K/V through its L2 at a time.
@@ -240,55 +240,65 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 
   // Block row max in log2 units (-inf: no legal key in the block; the scale
   // factor c is positive, so -inf * c stays -inf).
-  auto block_max = [&](const f32x4 (&s)[4][2], float (&mb)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
-      mx = max3f(mx, s[0][t][3], s[1][t][0]);
-      mx = max3f(mx, s[1][t][1], s[1][t][2]);
-      mx = max3f(mx, s[1][t][3], s[2][t][0]);
-      mx = max3f(mx, s[2][t][1], s[2][t][2]);
-      mx = max3f(mx, s[2][t][3], s[3][t][0]);
-      mx = max3f(mx, s[3][t][1], s[3][t][2]);
-      mx = max2f(mx, s[3][t][3]);
-      mb[t] = group4_max(mx) * c;
-    }
+  // Column max over the block in log2 units (-inf: no legal key; c > 0 keeps
+  // -inf * c at -inf): per-lane v_max3 chain, then the four lane groups.
+  auto block_max = [&](const f32x4 (&s)[4][2], int t) {
+    float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
+    mx = max3f(mx, s[0][t][3], s[1][t][0]);
+    mx = max3f(mx, s[1][t][1], s[1][t][2]);
+    mx = max3f(mx, s[1][t][3], s[2][t][0]);
+    mx = max3f(mx, s[2][t][1], s[2][t][2]);
+    mx = max3f(mx, s[2][t][3], s[3][t][0]);
+    mx = max3f(mx, s[3][t][1], s[3][t][2]);
+    mx = max2f(mx, s[3][t][3]);
+    return group4_max(mx) * c;
   };
 
-  // Online softmax update from the block max: moves the lazy reference when
-  // some lane of the wave needs it (rescaling row sums and accumulators), then
-  // turns the scores into bf16 weights in pf and adds them to the row sums.
-  // A row whose reference is still -inf has only -inf scores here (a legal
-  // key would have moved it), so its offset is taken as 0 to give 2^-inf = 0.
-  auto softmax = [&](f32x4 (&s)[4][2], const float (&mb)[2], bf16x8 (&pf)[2][2]) {
-    const bool need = (mb[0] > m_run[0] + kLazyRescale) || (mb[1] > m_run[1] + kLazyRescale);
+  // Online softmax of one block (scores s -> bf16 weights pf).  The weights
+  // are first formed against the current reference m (lazy: it moves only
+  // when needed).  If every lane's partial row sum over its 16 keys is at
+  // most 2^kLazyRescale, no weight exceeds that bound and the reference
+  // stays; no block max is computed.  Otherwise, or while a row has no
+  // reference yet, the column max moves the reference, the accumulators are
+  // rescaled and the weights recomputed (rare: a few blocks per row).
+  auto softmax = [&](const f32x4 (&s)[4][2], bf16x8 (&pf)[2][2]) {
+    f32x4 e[4][2];
+    float rs[2];
+    auto weights = [&](int t) {
+      const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[i][t][r] = fast_exp2(fmaf(s[i][t][r], c, mneg));
+          sum += e[i][t][r];
+        }
+      }
+      rs[t] = sum;
+    };
+    weights(0);
+    weights(1);
+    constexpr float kBound = 256.f;  // 2^kLazyRescale
+    static_assert(kLazyRescale == 8.f, "kBound is 2^kLazyRescale");
+    const bool need = !(rs[0] <= kBound) || !(rs[1] <= kBound) || m_run[0] == -INFINITY || m_run[1] == -INFINITY;
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const float mnew = fmaxf(m_run[t], mb[t]);
+        const float mnew = fmaxf(m_run[t], block_max(s, t));
         const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
         m_run[t] = mnew;
         l_run[t] *= alpha;
 #pragma unroll
         for (int j = 0; j < S::JV; ++j) acc[j][t] *= alpha;
+        weights(t);
       }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = fast_exp2(fmaf(s[i][t][r], c, mneg));
-          s[i][t][r] = e;
-          rs += e;
-        }
-      }
-      l_run[t] += rs;
-      pf[t][0] = pack_bf16x8(s[0][t], s[1][t]);
-      pf[t][1] = pack_bf16x8(s[2][t], s[3][t]);
+      l_run[t] += rs[t];
+      pf[t][0] = pack_bf16x8(e[0][t], e[1][t]);
+      pf[t][1] = pack_bf16x8(e[2][t], e[3][t]);
     }
   };
 
@@ -341,10 +351,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       av[0][0] = read_v(0, 0);
       av[0][1] = read_v(0, 1);
       __builtin_amdgcn_sched_barrier(0);
-      float mb[2];
-      block_max(s, mb);
       bf16x8 pf[2][2];
-      softmax(s, mb, pf);
+      softmax(s, pf);
       __builtin_amdgcn_sched_barrier(0);
       // O^T += V^T P^T over two 32-key halves, two dv tiles per step with the
       // next step's fragments in flight.  The contraction index e of the B

@@ -128,8 +128,9 @@ def cpu_baseline(probs, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first: the GPU clock settles under sustained load (about 0.5 s)")
     ap.add_argument("--workload", choices=["step", "prefill", "decode", "copy"], default="step",
                     help="time the whole step (default), one of its two calls alone (for profiling), or a "
                          "plain 1 GiB device copy (to calibrate the HBM byte counters)")

@@ -192,3 +192,34 @@ def test_streams_are_honoured(orc):
     o, lse = outs.host()
     ro, rl = orc.fwd(q, k, v)
     compare(o, lse, ro, rl, "bf16", "side stream")
+
+
+def _shape_keys(k, pattern):
+    """Rescale key rows so the running row max moves many times (growing),
+    once early then never (decaying), or at isolated spikes."""
+    kf = inputs.bf16_bits_to_f32(k).astype(np.float64)
+    K = kf.shape[2]
+    j = np.arange(K, dtype=np.float64)
+    if pattern == "growing":
+        f = 0.25 + 6.0 * j / max(K - 1, 1)
+    elif pattern == "decaying":
+        f = 6.0 - 5.75 * j / max(K - 1, 1)
+    else:  # spikes
+        f = np.full(K, 0.5)
+        f[(j % 97) == 13] = 8.0
+    kf = kf * f[None, None, :, None]
+    return inputs.f32_to_bf16_bits(kf.astype(np.float32))
+
+
+@pytest.mark.parametrize("pattern", ["growing", "decaying", "spikes"])
+@pytest.mark.parametrize("Q", [1, 4, 200])
+def test_running_max_moves(orc, pattern, Q):
+    """Score ranges that force the lazy reference to move many times, once, or
+    at isolated keys (weights up to 2^8 against a stale reference)."""
+    w = inputs.Workload("maxmoves", 2, 8, 2, Q, 1500, 128, 128, seqlens=np.array([1500, 1111], np.int32))
+    q, v = w.gen_q(), w.gen_v()
+    k = _shape_keys(w.gen_k(), pattern)
+    say(f"[case] running max {pattern} Q={Q}")
+    o, lse = run_gpu(w, q, k, v, scale=0.3)
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, scale=0.3)
+    compare(o, lse, ro, rl, "bf16", f"running max {pattern}")
