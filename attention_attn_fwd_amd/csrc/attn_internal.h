@@ -24,6 +24,7 @@ constexpr int kDecodeSub = 32;
 constexpr int kDecodeChunkAlign = kDecodeSub;
 constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
 constexpr int kDecodeMaxQ = 4;
+constexpr int kDecodeStages = 2;  // LDS ring depth of the split kernel (sub-blocks)
 
 // fp32 path: one workgroup of 256 threads per (batch, head, 32 query rows).
 constexpr int kF32Rows = 32;
@@ -134,6 +135,19 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 __device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
 __device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
+
+// Reductions over the whole wave (butterfly with DPP-free shuffles).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x = max2f(x, __shfl_xor(x, o));
+  return group4_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+  return group4_sum(x);
+}
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

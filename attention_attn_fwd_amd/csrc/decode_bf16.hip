@@ -22,8 +22,9 @@
 
 namespace attn {
 
-template <int DP, int DVP, int NT>
+template <int DP, int DVP, int NT, int NSTG = kDecodeStages>
 struct DecodeShape {
+  static constexpr int NS = NSTG;               // ring stages (sub-blocks in LDS)
   static constexpr int KS = DP / 32;
   static constexpr int JV = DVP / 16;
   static constexpr int KCH = DP / 8;            // 16-byte chunks per K row
@@ -49,14 +50,13 @@ __device__ __forceinline__ void group_key_range(int Kb, int Q, int W, int* lo, i
 template <int DP, int DVP, int NT>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   using S = DecodeShape<DP, DVP, NT>;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[S::NS * S::STAGE];
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Items (chunk, batch, kv-head) are numbered chunk-slowest, so the leading
-  // chunks of every sequence are dispatched first and the workgroups of chunks
-  // past a sequence's end (which return after one length lookup) come last.
-  // The launch has one workgroup per item; the loop also serves a smaller grid.
+  // Items (chunk, batch, kv-head) are numbered with the chunk slowest (see
+  // below for its order).  The launch has one workgroup per item; the loop
+  // also serves a smaller grid.
   const int groups = p.B * p.Hkv;
   const int n_items = p.n_splits * groups;
 
@@ -79,13 +79,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   }
 
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-  const int chunk = item / groups;
-  const int b = (item - chunk * groups) / p.Hkv;
-  const int kh = item - chunk * groups - b * p.Hkv;
+  const int ri = item / groups;
+  const int b = (item - ri * groups) / p.Hkv;
+  const int kh = item - ri * groups - b * p.Hkv;
   const int Kb = clamp_len(p.seqlens, b, p.K);
   const int Q = p.Q, W = p.window, delta = Kb - Q;
   int lo_u, hi_u;
   group_key_range(Kb, Q, W, &lo_u, &hi_u);
+  if (hi_u <= lo_u) continue;  // no key: the combine pass writes 0 / -inf
+  // Items are counted back from each sequence's last chunk, the slowest
+  // index running from the most distant chunk to the last: the workgroups
+  // dispatched last take the sequences' final (partial) chunks, so the
+  // kernel's tail is short.
+  const int c_last = (hi_u - 1) / p.chunk;
+  const int chunk = c_last - (p.n_splits - 1 - ri);
+  if (chunk < lo_u / p.chunk) continue;
   const int cs = chunk * p.chunk;
   const int ce = min(cs + p.chunk, hi_u);
   const int st = max(cs, lo_u);
@@ -150,20 +158,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 
   const int j0 = (st - cs) / kDecodeSub;
   const int j1 = (ce - cs + kDecodeSub - 1) / kDecodeSub;
-  issue(j0, 0);
-  if (j0 + 1 < j1) issue(j0 + 1, 1);
+#pragma unroll
+  for (int u = 0; u < S::NS; ++u)
+    if (j0 + u < j1) issue(j0 + u, u);
 
   // Absolute position of each packed row (row rr is query rr % Q).
   int pq[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) pq[t] = (16 * t + l16) % Q + delta;
 
-  // Sub-block j sits in stage (j - j0) % 2; once every LDS read of it has
-  // returned, sub-block j + 2 is issued into the same stage.
+  // Sub-block j sits in stage (j - j0) % NS; once every LDS read of it has
+  // returned, sub-block j + NS is issued into the same stage.  Before
+  // computing j, the loads of the up to NS - 1 later sub-blocks may stay in
+  // flight.
   int stg = 0;
   for (int j = j0; j < j1; ++j) {
-    if (j + 1 < j1) wait_vmcnt<S::LOADS>();
-    else wait_vmcnt<0>();
+    const int later = min(S::NS - 1, j1 - 1 - j);
+    static_for<S::NS>([&](auto n_tag) {
+      constexpr int n = decltype(n_tag)::value;
+      if (later == n) wait_vmcnt<n * S::LOADS>();
+    });
     const unsigned char* kst = ring + stg * S::STAGE;
     const unsigned char* vst = kst + S::K_STAGE;
     const int kb0 = cs + j * kDecodeSub;
@@ -259,11 +273,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     for (int jv = 0; jv < S::JV; ++jv)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(vf[jv], pf[t], acc[jv][t]);
-    if (j + 2 < j1) {
+    if (j + S::NS < j1) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(j + 2, stg);
+      issue(j + S::NS, stg);
     }
-    stg ^= 1;
+    stg = stg + 1 == S::NS ? 0 : stg + 1;
   }
 
   // One partial per (row, chunk): m in log2 units, l = sum of 2^(s*c - m), unnormalised acc.
@@ -290,6 +304,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 }
 
 // One wave per output row (b, h, q): merge the row's partials in chunk order.
+// Lane c holds chunk c's (m, l) (64 chunks per round), so the row max and
+// the weights f_c = 2^(m_c - M) take one round of loads and a wave
+// reduction; then every lane accumulates two dv columns over the chunks with
+// all of a round's loads in flight.  The merge order is fixed, so results
+// are bitwise reproducible.
 __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row_id = (int64_t)blockIdx.x * 4 + wave;
@@ -308,20 +327,43 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int64_t split0 = ((int64_t)b * p.Hkv + kh) * p.n_splits;
   const int R = p.rows;
 
+  // Row max over the chunks (a chunk with no legal key for this row has m = -inf).
   float M = -INFINITY;
-  for (int cix = c_lo; cix < c_hi; ++cix) M = fmaxf(M, p.ws_m[(split0 + cix) * R + rr]);
+  for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+    const int cix = c0 + lane;
+    const float m = cix < c_hi ? p.ws_m[(split0 + cix) * R + rr] : -INFINITY;
+    M = fmaxf(M, m);
+  }
+  M = wave_max(M);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
   if (M != -INFINITY) {
-    for (int cix = c_lo; cix < c_hi; ++cix) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+      const int cix = c0 + lane;
       const int64_t sp = (split0 + cix) * R + rr;
-      const float m = p.ws_m[sp];
-      if (m == -INFINITY) continue;
-      const float f = fast_exp2(m - M);
-      L += p.ws_l[sp] * f;
-      const float* a = p.ws_acc + sp * p.Dv;
-      if (lane < p.Dv) o0 += a[lane] * f;
-      if (lane + 64 < p.Dv) o1 += a[lane + 64] * f;
+      const float m = cix < c_hi ? p.ws_m[sp] : -INFINITY;
+      const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
+      L += cix < c_hi ? p.ws_l[sp] * f : 0.f;
+      const int n = min(64, c_hi - c0);
+      // Lane `u` of the round holds f for chunk c0 + u.
+      constexpr int U = 8;
+      for (int u0 = 0; u0 < n; u0 += U) {
+        float a0[U], a1[U], fu[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = u0 + u < n;
+          const float* a = p.ws_acc + ((split0 + c0 + u0 + u) * R + rr) * p.Dv;
+          a0[u] = ok && lane < p.Dv ? a[lane] : 0.f;
+          a1[u] = ok && lane + 64 < p.Dv ? a[lane + 64] : 0.f;
+          fu[u] = __shfl(f, (u0 + u) & 63);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          o0 = fmaf(a0[u], fu[u], o0);
+          o1 = fmaf(a1[u], fu[u], o1);
+        }
+      }
     }
+    L = wave_sum(L);
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + row_id * p.Dv;
