@@ -29,7 +29,7 @@ class AttnError(RuntimeError):
 
 
 class _Plan(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int), ("split_chunk", ctypes.c_int), ("n_splits", ctypes.c_int),
+    _fields_ = [("path", ctypes.c_int), ("split_workers", ctypes.c_int), ("partial_slots", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_int64)]
 
 
@@ -98,7 +98,7 @@ def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
     st = load().attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, int(window), ctypes.byref(plan))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_plan")
-    return {"path": plan.path, "split_chunk": plan.split_chunk, "n_splits": plan.n_splits,
+    return {"path": plan.path, "split_workers": plan.split_workers, "partial_slots": plan.partial_slots,
             "workspace_bytes": plan.workspace_bytes}
 
 

@@ -2,6 +2,7 @@
 // launch planning, stream-ordered scratch for the split-KV path, launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -57,21 +58,24 @@ bool supported_width(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Keys per split for the decode path: the smallest power of two >= 256 that
-// keeps the grid within 8192 single-wave workgroups at full length (dozens per
-// CU, so the uneven lengths of a batch balance out, while each workgroup
-// streams long enough to amortise its start), capped at 4096 keys.
-// ATTN_FWD_SPLIT_CHUNK (a multiple of 32) overrides it.
-int split_chunk(int B, int Hkv, int K) {
-  if (const char* e = std::getenv("ATTN_FWD_SPLIT_CHUNK")) {
+// Workers of the split-KV pass: as many single-wave workgroups as are
+// resident at once (four per CU of the 256, fewer when the two LDS ring
+// stages of K, V and Q sub-blocks need more than 40 KiB), fewer still when
+// even the padded length gives less than kDecodeMinShare sub-blocks each.
+// ATTN_FWD_SPLIT_WORKERS (>= 1) overrides it.
+int split_workers(int B, int Hkv, int K, int D, int Dv, int rows) {
+  if (K <= 0) return 0;
+  if (const char* e = std::getenv("ATTN_FWD_SPLIT_WORKERS")) {
     const int v = std::atoi(e);
-    if (v >= kDecodeChunkAlign && v % kDecodeChunkAlign == 0) return v;
+    if (v >= 1) return v;
   }
-  const int64_t groups = (int64_t)B * Hkv;
-  const int64_t target = 8192;
-  int ch = 256;
-  while (ch < 4096 && groups * ((K + ch - 1) / ch) > target) ch *= 2;
-  return ch;
+  const int dp = pad_width(D), dvp = pad_width(Dv), qrows = rows <= 16 ? 16 : 32;
+  const int stage = kDecodeSub * (dp + dvp) * 2 + qrows * dp * 2;
+  const int per_cu = std::min(4, 160 * 1024 / (2 * stage));
+  const int64_t resident = (int64_t)per_cu * 256;
+  const int64_t sub = (int64_t)B * Hkv * ((K + kDecodeSub - 1) / kDecodeSub);
+  const int64_t w = (sub + kDecodeMinShare - 1) / kDecodeMinShare;
+  return (int)std::max<int64_t>(1, std::min(w, resident));
 }
 
 // Checks shared by both entry points; fills the plan.
@@ -94,9 +98,9 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   const int group = Hq / Hkv;
   if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows) {
     plan->path = 2;
-    plan->split_chunk = split_chunk(B, Hkv, K);
-    plan->n_splits = K > 0 ? (K + plan->split_chunk - 1) / plan->split_chunk : 0;
-    const int64_t parts = (int64_t)B * Hkv * plan->n_splits * group * Q;
+    plan->split_workers = split_workers(B, Hkv, K, D, Dv, group * Q);
+    plan->partial_slots = plan->split_workers > 0 ? B * Hkv + plan->split_workers : 0;
+    const int64_t parts = (int64_t)plan->partial_slots * group * Q;
     plan->workspace_bytes = parts * (int64_t)(Dv + 2) * 4;
   } else {
     plan->path = 1;
@@ -134,9 +138,8 @@ int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* 
   if (plan.path == 1) return launch_status(launch_prefill_bf16(p, stream));
 
   // Split-KV decode: scratch from the device's stream-ordered pool.
-  p.chunk = plan.split_chunk;
-  p.n_splits = plan.n_splits;
-  const int64_t parts = (int64_t)B * Hkv * plan.n_splits * p.rows;
+  p.n_workers = plan.split_workers;
+  const int64_t parts = (int64_t)plan.partial_slots * p.rows;
   const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
   if (fail && fail[0] == '1') return ATTN_ERR_OOM;
   void* ws = nullptr;

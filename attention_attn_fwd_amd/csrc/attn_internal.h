@@ -18,13 +18,13 @@ constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // query rows per workgroup
 constexpr int kPrefillBN = 64;                                   // keys per block
 
-// Split-KV decode: single-wave workgroups streaming 32-key sub-blocks; chunks
-// are multiples of 32 keys so every sub-block lies inside one chunk.
+// Split-KV decode: single-wave workers streaming 32-key sub-blocks, each an
+// equal share of all (batch, kv-head) groups' sub-blocks.
 constexpr int kDecodeSub = 32;
-constexpr int kDecodeChunkAlign = kDecodeSub;
 constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
 constexpr int kDecodeMaxQ = 4;
-constexpr int kDecodeStages = 2;  // LDS ring depth of the split kernel (sub-blocks)
+// Each worker of the split pass takes at least kDecodeMinShare sub-blocks.
+constexpr int kDecodeMinShare = 4;
 
 // fp32 path: one workgroup of 256 threads per (batch, head, 32 query rows).
 constexpr int kF32Rows = 32;
@@ -43,12 +43,11 @@ struct Params {
   int q_sign;              // 0x8000 when the scale is negative (q is negated), else 0
   float scale_log2;        // |scale| * log2(e)
   float scale;             // raw scale (fp32 path)
-  // split-KV decode scratch
-  float* ws_m;             // [B][Hkv][n_splits][rows]  running max, log2 units
-  float* ws_l;             // [B][Hkv][n_splits][rows]  sum of 2^(s*c - m)
-  float* ws_acc;           // [B][Hkv][n_splits][rows][Dv] unnormalised P.V
-  int chunk;               // keys per split (multiple of kDecodeChunkAlign)
-  int n_splits;            // ceil(K / chunk)
+  // split-KV decode scratch: one partial per (slot, row), slot = group + worker
+  float* ws_m;             // [slots][rows]  running max, log2 units
+  float* ws_l;             // [slots][rows]  sum of 2^(s*c - m)
+  float* ws_acc;           // [slots][rows][Dv] unnormalised P.V
+  int n_workers;           // workgroups of the split pass (0: no keys at all)
   int rows;                // group * Q
 };
 

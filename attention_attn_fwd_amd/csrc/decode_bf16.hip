@@ -6,37 +6,50 @@
 // of that state, which is what the combine pass does, and that one kv-head
 // serves Hq/Hkv query heads; section 4 notes that a single query row cannot
 // fill a matrix atom.  Hence:
-//   * one single-wave workgroup per (chunk of keys, kv-head, batch); the g*Q
-//     query rows of the kv-head's group are packed as the 16-wide N side of
-//     v_mfma_f32_16x16x32_bf16 and keys are the M side, so K and V are read
-//     from HBM once per (batch, kv-head);
-//   * the chunk streams through a two-stage LDS ring of 32-key sub-blocks
-//     filled by direct buffer-to-LDS loads: while sub-block j is computed the
-//     loads of j+1 are in flight, and j+2 is issued as soon as j is consumed;
-//     rows past K_b and channels past D read as zero from the buffer range
-//     check, so the loads have no branches;
-//   * each workgroup writes one fp32 partial (m, l, acc[Dv]) per row;
-//   * the combine pass merges a row's partials in chunk order, so results are
-//     bitwise reproducible (no atomics).
+//   * the g*Q query rows of a (batch, kv-head) group are packed as the 16-wide
+//     N side of v_mfma_f32_16x16x32_bf16 and keys are the M side, so K and V
+//     are read from HBM once per group;
+//   * the work is cut stream-K fashion: every group's legal key range is a
+//     run of 32-key sub-blocks, the runs of all groups are laid end to end,
+//     and each of a fixed number of single-wave workers takes an equal
+//     contiguous share.  A worker streams its share without a break, across
+//     group boundaries, so all workers finish together and no worker waits
+//     for a dispatch: with one workgroup per fixed-size chunk, a batch of
+//     uneven lengths left the GPU half idle for the last third of the pass;
+//   * a worker streams through a two-stage LDS ring of sub-blocks filled by
+//     direct buffer-to-LDS loads; the sub-block that opens a group in the
+//     worker's share also carries that group's Q rows in its stage, so the Q
+//     of the next group arrives in order with its keys; rows past K_b and
+//     channels past D read as zero from the buffer range check;
+//   * a worker writes one fp32 partial (m, l, acc[Dv]) per row for each group
+//     piece it processed, at partial slot (group + worker): the pieces of
+//     group g come from workers first(g)..last(g), so slots g + w never
+//     collide and there are at most groups + workers of them;
+//   * the combine pass recomputes the same partition and merges a row's
+//     partials in worker order, so results are bitwise reproducible (no
+//     atomics).
 #include "attn_internal.h"
 
 namespace attn {
 
-template <int DP, int DVP, int NT, int NSTG = kDecodeStages>
+template <int DP, int DVP, int NT>
 struct DecodeShape {
-  static constexpr int NS = NSTG;               // ring stages (sub-blocks in LDS)
   static constexpr int KS = DP / 32;
   static constexpr int JV = DVP / 16;
   static constexpr int KCH = DP / 8;            // 16-byte chunks per K row
   static constexpr int VCH = DVP / 8;
-  static constexpr int KROWB = DP * 2;          // LDS bytes per K row
+  static constexpr int KROWB = DP * 2;          // LDS bytes per K (and Q) row
   static constexpr int VROWB = DVP * 2;
   static constexpr int K_STAGE = kDecodeSub * KROWB;
   static constexpr int V_STAGE = kDecodeSub * VROWB;
-  static constexpr int STAGE = K_STAGE + V_STAGE;
+  static constexpr int QROWS = 16 * NT;         // packed query rows (N side)
+  static constexpr int Q_STAGE = QROWS * KROWB;
+  static constexpr int STAGE = K_STAGE + V_STAGE + Q_STAGE;
   static constexpr int K_LOADS = K_STAGE / 1024;  // wave-wide 1 KiB loads per stage
   static constexpr int V_LOADS = V_STAGE / 1024;
+  static constexpr int Q_LOADS = Q_STAGE / 1024;
   static constexpr int LOADS = K_LOADS + V_LOADS;
+  static_assert(Q_STAGE % 1024 == 0 && Q_LOADS <= K_LOADS, "Q tile uses the first K load offsets");
 };
 
 // Union of the legal key ranges of all rows of one (batch, kv-head) group:
@@ -47,23 +60,137 @@ __device__ __forceinline__ void group_key_range(int Kb, int Q, int W, int* lo, i
   *lo = W > 0 ? max(0, Kb - Q - W + 1) : 0;
 }
 
+// A sequence's groups: key range [lo, hi) with hi = K_b, and nsb sub-blocks.
+struct SeqRange {
+  int lo, hi, nsb;
+};
+__device__ __forceinline__ SeqRange seq_range(const Params& p, int b) {
+  const int Kb = clamp_len(p.seqlens, b, p.K);
+  int lo, hi;
+  group_key_range(Kb, p.Q, p.window, &lo, &hi);
+  return SeqRange{lo, hi, hi > lo ? (hi - lo + kDecodeSub - 1) / kDecodeSub : 0};
+}
+
+// Sub-blocks of sequence b (all its kv-head groups) as the lane's value of a
+// wave-wide pass over sequences b0 + lane.
+__device__ __forceinline__ int64_t seq_subblocks(const Params& p, int b) {
+  return b < p.B ? (int64_t)seq_range(p, b).nsb * p.Hkv : 0;
+}
+
+// A wave-uniform 64-bit value the compiler can keep in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Total sub-blocks over all groups (wave-uniform).
+__device__ __forceinline__ int64_t total_subblocks(const Params& p, int lane) {
+  int64_t tot = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) tot += __shfl(wave_incl_scan(seq_subblocks(p, b0 + lane), lane), 63);
+  return uniform64(tot);
+}
+
+// First global sub-block of sequence b's groups (sum over earlier sequences).
+__device__ __forceinline__ int64_t seq_base(const Params& p, int b, int lane) {
+  int64_t base = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    const int bb = b0 + lane;
+    base += __shfl(wave_incl_scan(bb < b ? seq_subblocks(p, bb) : 0, lane), 63);
+  }
+  return uniform64(base);
+}
+
+// Per-row share of the stream-K partition: sub-blocks per worker.
+__device__ __forceinline__ int64_t worker_share(int64_t total, int workers) {
+  return (total + workers - 1) / workers;
+}
+
+// Position of one sub-block in the partition (wave-uniform; the fields are
+// passed through readfirstlane so descriptors built from them are scalar).
+struct Cursor {
+  int b, kh, sb;  // sequence, kv-head, sub-block within the group
+  int nsb, lo, Kb;
+};
+__device__ __forceinline__ void make_uniform(Cursor& c) {
+  c.b = __builtin_amdgcn_readfirstlane(c.b);
+  c.kh = __builtin_amdgcn_readfirstlane(c.kh);
+  c.sb = __builtin_amdgcn_readfirstlane(c.sb);
+  c.nsb = __builtin_amdgcn_readfirstlane(c.nsb);
+  c.lo = __builtin_amdgcn_readfirstlane(c.lo);
+  c.Kb = __builtin_amdgcn_readfirstlane(c.Kb);
+}
+
 template <int DP, int DVP, int NT>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   using S = DecodeShape<DP, DVP, NT>;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[S::NS * S::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
 
   const int lane = threadIdx.x;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // Items (chunk, batch, kv-head) are numbered with the chunk slowest (see
-  // below for its order).  The launch has one workgroup per item; the loop
-  // also serves a smaller grid.
-  const int groups = p.B * p.Hkv;
-  const int n_items = p.n_splits * groups;
+  const int w = blockIdx.x;
+
+  const int64_t T = total_subblocks(p, lane);
+  const int64_t per = worker_share(T, p.n_workers);
+  const int64_t s0 = (int64_t)w * per;
+  const int64_t s1 = min(T, s0 + per);
+  if (s0 >= s1) return;
+  const int n = (int)(s1 - s0);
+
+  // Cursor of global sub-block s0.
+  Cursor start;
+  {
+    int64_t run = 0;
+    for (int b0 = 0;; b0 += 64) {
+      const int64_t cnt = seq_subblocks(p, b0 + lane);
+      const int64_t incl = wave_incl_scan(cnt, lane);
+      const int64_t tot = uniform64(__shfl(incl, 63));
+      if (s0 < run + tot) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(run + incl > s0);
+        const int first = __builtin_ctzll(m);
+        const int b = b0 + first;
+        const int64_t base = uniform64(run + __shfl(incl - cnt, first));
+        const SeqRange r = seq_range(p, b);
+        const int64_t off = s0 - base;
+        start = Cursor{b, (int)(off / r.nsb), (int)(off % r.nsb), r.nsb, r.lo, r.hi};
+        make_uniform(start);
+        break;
+      }
+      run += tot;
+    }
+  }
+  // Next sub-block of the partition (only called while one exists).
+  auto advance = [&](Cursor& c) {
+    if (++c.sb < c.nsb) return;
+    c.sb = 0;
+    if (++c.kh < p.Hkv) return;
+    c.kh = 0;
+    SeqRange r;
+    do {
+      ++c.b;
+      r = seq_range(p, c.b);
+    } while (r.nsb == 0);
+    c.nsb = r.nsb;
+    c.lo = r.lo;
+    c.Kb = r.hi;
+    make_uniform(c);
+  };
 
   // This lane's byte offset, from the start of a sub-block, for each 1 KiB
-  // direct load of a stage: load i fills stage bytes [1024 i, 1024 i + 1024),
+  // direct load of a stage: load i fills tile bytes [1024 i, 1024 i + 1024),
   // lane l position l of it, which holds chunk (position ^ swizzle) of its row.
-  // Chunks past D (Dv) get an offset beyond any buffer and read as zero.
+  // Chunks past D (Dv) get an offset beyond any buffer and read as zero.  The
+  // Q tile has the K tile's layout, so it uses the first Q_LOADS K offsets.
   uint32_t koff[S::K_LOADS], voff[S::V_LOADS];
 #pragma unroll
   for (int i = 0; i < S::K_LOADS; ++i) {
@@ -78,109 +205,88 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     voff[i] = ch < p.Dv / 8 ? (uint32_t)(row * p.Dv + ch * 8) * 2 : kOutOfRange;
   }
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-  const int ri = item / groups;
-  const int b = (item - ri * groups) / p.Hkv;
-  const int kh = item - ri * groups - b * p.Hkv;
-  const int Kb = clamp_len(p.seqlens, b, p.K);
-  const int Q = p.Q, W = p.window, delta = Kb - Q;
-  int lo_u, hi_u;
-  group_key_range(Kb, Q, W, &lo_u, &hi_u);
-  if (hi_u <= lo_u) continue;  // no key: the combine pass writes 0 / -inf
-  // Items are counted back from each sequence's last chunk, the slowest
-  // index running from the most distant chunk to the last: the workgroups
-  // dispatched last take the sequences' final (partial) chunks, so the
-  // kernel's tail is short.
-  const int c_last = (hi_u - 1) / p.chunk;
-  const int chunk = c_last - (p.n_splits - 1 - ri);
-  if (chunk < lo_u / p.chunk) continue;
-  const int cs = chunk * p.chunk;
-  const int ce = min(cs + p.chunk, hi_u);
-  const int st = max(cs, lo_u);
-  if (st >= ce) continue;  // the combine pass never reads this split
-  // The previous item's reads of the ring have returned before it is refilled.
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-
-  const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
-  const uint16_t* kslice = static_cast<const uint16_t*>(p.k) + kv_slice * p.K * p.D;
-  const uint16_t* vslice = static_cast<const uint16_t*>(p.v) + kv_slice * p.K * p.Dv;
-  const float c = p.scale_log2;
-  const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
-
-  // Q^T fragments: N column l16 of tile t is packed row rr = hh*Q + q.
-  bf16x8 qf[NT][S::KS];
+  const int R = p.rows;
+  const uint32_t ring0 = lds_offset(ring);
+  // Loads of the sub-block at cursor c into stage stg; with_q adds the Q rows
+  // of c's group (rows past R read as zero).
+  auto issue = [&](const Cursor& c, int stg, bool with_q) {
+    const int kb0 = c.lo + c.sb * kDecodeSub;
+    const int64_t kv_slice = (int64_t)c.b * p.Hkv + c.kh;
+    const uint32_t rows_left = (uint32_t)(c.Kb - kb0);
+    const rsrc_t krs =
+        slice_rsrc(static_cast<const uint16_t*>(p.k) + (kv_slice * p.K + kb0) * p.D, rows_left * p.D * 2);
+    const rsrc_t vrs =
+        slice_rsrc(static_cast<const uint16_t*>(p.v) + (kv_slice * p.K + kb0) * p.Dv, rows_left * p.Dv * 2);
+    const uint32_t st = ring0 + stg * S::STAGE;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int rr = 16 * t + l16;
-    const bool ok = rr < p.rows;
-    const int hh = ok ? rr / Q : 0, qi = ok ? rr % Q : 0;
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.Hq + kh * p.group + hh) * Q + qi) * p.D;
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(krs, st + i * 1024, koff[i]);
 #pragma unroll
-    for (int s = 0; s < S::KS; ++s) {
-      const int col = 32 * s + 8 * g4;
-      uint4 u = (ok && col < p.D) ? load_u4(qrow + col) : zero_u4();
-      u.x ^= qx; u.y ^= qx; u.z ^= qx; u.w ^= qx;
-      qf[t][s] = __builtin_bit_cast(bf16x8, u);
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(vrs, st + S::K_STAGE + i * 1024, voff[i]);
+    if (with_q) {
+      const rsrc_t qrs = slice_rsrc(
+          static_cast<const uint16_t*>(p.q) + ((int64_t)c.b * p.Hq + c.kh * p.group) * p.Q * p.D, (uint32_t)R * p.D * 2);
+#pragma unroll
+      for (int i = 0; i < S::Q_LOADS; ++i) load_lds16(qrs, st + S::K_STAGE + S::V_STAGE + i * 1024, koff[i]);
     }
-  }
-  // Q is in registers before any direct load is issued.
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int s = 0; s < S::KS; ++s) launder(qf[t][s]);
-
-  float m_run[NT], l_run[NT];
-  f32x4 acc[S::JV][NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-#pragma unroll
-    for (int j = 0; j < S::JV; ++j) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Issue the direct loads of sub-block j into ring stage `stg`.  The buffer
-  // descriptors start at the sub-block and end at K_b, so the per-lane offsets
-  // are the same for every sub-block and rows past K_b read as zero.
-  auto issue = [&](int j, int stg) {
-    const int kb0 = cs + j * kDecodeSub;
-    const uint32_t rows_left = (uint32_t)(Kb - kb0);
-    const rsrc_t krs = slice_rsrc(kslice + (int64_t)kb0 * p.D, rows_left * p.D * 2);
-    const rsrc_t vrs = slice_rsrc(vslice + (int64_t)kb0 * p.Dv, rows_left * p.Dv * 2);
-    const uint32_t kst = lds_offset(ring) + stg * S::STAGE;
-#pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(krs, kst + i * 1024, koff[i]);
-#pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(vrs, kst + S::K_STAGE + i * 1024, voff[i]);
   };
 
-  const int j0 = (st - cs) / kDecodeSub;
-  const int j1 = (ce - cs + kDecodeSub - 1) / kDecodeSub;
-#pragma unroll
-  for (int u = 0; u < S::NS; ++u)
-    if (j0 + u < j1) issue(j0 + u, u);
+  const float c = p.scale_log2;
+  const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
+  const int W = p.window, Qn = p.Q;
 
-  // Absolute position of each packed row (row rr is query rr % Q).
-  int pq[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) pq[t] = (16 * t + l16) % Q + delta;
+  bf16x8 qf[NT][S::KS];
+  float m_run[NT], l_run[NT];
+  f32x4 acc[S::JV][NT];
 
-  // Sub-block j sits in stage (j - j0) % NS; once every LDS read of it has
-  // returned, sub-block j + NS is issued into the same stage.  Before
-  // computing j, the loads of the up to NS - 1 later sub-blocks may stay in
-  // flight.
+  // Prologue: the first two sub-blocks; each stage remembers whether it
+  // carries Q (a group opens there), which fixes its number of loads.
+  Cursor cc = start, ic = start;
+  bool stage_q[2] = {false, false};
+  issue(ic, 0, true);
+  stage_q[0] = true;
+  if (n > 1) {
+    advance(ic);
+    stage_q[1] = ic.sb == 0;
+    issue(ic, 1, stage_q[1]);
+  }
+
   int stg = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int later = min(S::NS - 1, j1 - 1 - j);
-    static_for<S::NS>([&](auto n_tag) {
-      constexpr int n = decltype(n_tag)::value;
-      if (later == n) wait_vmcnt<n * S::LOADS>();
-    });
+  for (int j = 0; j < n; ++j) {
+    // Sub-block j's loads have landed; those of j + 1 may stay in flight.
+    if (j + 1 < n) {
+      if (stage_q[stg ^ 1]) wait_vmcnt<S::LOADS + S::Q_LOADS>();
+      else wait_vmcnt<S::LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
     const unsigned char* kst = ring + stg * S::STAGE;
     const unsigned char* vst = kst + S::K_STAGE;
-    const int kb0 = cs + j * kDecodeSub;
+    const bool opens = stage_q[stg];  // first sub-block of a group in this share
+    const int Kb = cc.Kb, delta = Kb - Qn;
+    const int kb0 = cc.lo + cc.sb * kDecodeSub;
+
+    if (opens) {
+      // Q^T fragments from the stage's Q tile: N column l16 of tile t is
+      // packed row 16t + l16 = hh*Q + q of the group.
+      const unsigned char* qst = vst + S::V_STAGE;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int row = 16 * t + l16;
+#pragma unroll
+        for (int s = 0; s < S::KS; ++s) {
+          uint4 u = *reinterpret_cast<const uint4*>(qst + row * S::KROWB + (((4 * s + g4) ^ swz_k<S::KCH>(row)) << 4));
+          u.x ^= qx; u.y ^= qx; u.z ^= qx; u.w ^= qx;
+          qf[t][s] = __builtin_bit_cast(bf16x8, u);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+#pragma unroll
+        for (int jv = 0; jv < S::JV; ++jv) acc[jv][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
 
     // Every LDS read of the sub-block is issued up front (K fragments, then the
     // transposed V fragments), so a single wave pays the LDS latency once per
@@ -225,12 +331,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     if (!full) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        const int pq = (16 * t + l16) % Qn + delta;  // absolute position of packed row
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int key = kb0 + 16 * i + 4 * g4 + r;
-            const bool legal = key <= pq[t] && key < Kb && (W <= 0 || key > pq[t] - W);
+            const bool legal = (key <= pq) & (key < Kb) & ((W <= 0) | (key > pq - W));
             if (!legal) sacc[i][t][r] = -INFINITY;
           }
         }
@@ -239,11 +346,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     bf16x8 pf[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float mx = sacc[0][t][0];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[i][t][r]);
+      float mx = max3f(sacc[0][t][0], sacc[0][t][1], sacc[0][t][2]);
+      mx = max3f(mx, sacc[0][t][3], sacc[1][t][0]);
+      mx = max3f(mx, sacc[1][t][1], sacc[1][t][2]);
+      mx = max2f(mx, sacc[1][t][3]);
       mx = group4_max(mx);
       const float mb = (mx == -INFINITY) ? -INFINITY : mx * c;
       float alpha;
@@ -252,15 +358,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 #pragma unroll
         for (int jv = 0; jv < S::JV; ++jv) acc[jv][t] *= alpha;
       }
-      const float mref = m_run[t];
+      const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float sv = sacc[i][t][r];
-          float e = fast_exp2(fmaf(sv, c, -mref));
-          if (!full) e = (sv == -INFINITY) ? 0.f : e;
+          const float e = fast_exp2(fmaf(sacc[i][t][r], c, mneg));
           sacc[i][t][r] = e;
           rs += e;
         }
@@ -273,42 +377,48 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     for (int jv = 0; jv < S::JV; ++jv)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(vf[jv], pf[t], acc[jv][t]);
-    if (j + S::NS < j1) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      issue(j + S::NS, stg);
-    }
-    stg = stg + 1 == S::NS ? 0 : stg + 1;
-  }
 
-  // One partial per (row, chunk): m in log2 units, l = sum of 2^(s*c - m), unnormalised acc.
-  const int64_t split = kv_slice * p.n_splits + chunk;
-  const int R = p.rows;
+    // The stage is free once its LDS reads have returned: refill it with
+    // sub-block j + 2.
+    if (j + 2 < n) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      advance(ic);
+      stage_q[stg] = ic.sb == 0;
+      issue(ic, stg, stage_q[stg]);
+    }
+
+    // The piece of the group ends with its last sub-block or the share's.
+    if (cc.sb == cc.nsb - 1 || j == n - 1) {
+      const int64_t slot = (int64_t)cc.b * p.Hkv + cc.kh + w;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float lt = group4_sum(l_run[t]);
-    const int rr = 16 * t + l16;
-    if (rr < R) {
-      const int64_t part = split * R + rr;
-      if (g4 == 0) {
-        p.ws_m[part] = m_run[t];
-        p.ws_l[part] = lt;
-      }
+      for (int t = 0; t < NT; ++t) {
+        const float lt = group4_sum(l_run[t]);
+        const int rr = 16 * t + l16;
+        if (rr < R) {
+          const int64_t part = slot * R + rr;
+          if (g4 == 0) {
+            p.ws_m[part] = m_run[t];
+            p.ws_l[part] = lt;
+          }
 #pragma unroll
-      for (int jv = 0; jv < S::JV; ++jv) {
-        const int dv = 16 * jv + 4 * g4;
-        if (dv < p.Dv) *reinterpret_cast<f32x4*>(p.ws_acc + part * p.Dv + dv) = acc[jv][t];
+          for (int jv = 0; jv < S::JV; ++jv) {
+            const int dv = 16 * jv + 4 * g4;
+            if (dv < p.Dv) *reinterpret_cast<f32x4*>(p.ws_acc + part * p.Dv + dv) = acc[jv][t];
+          }
+        }
       }
     }
+    if (j + 1 < n) advance(cc);
+    stg ^= 1;
   }
-  }  // items
 }
 
-// One wave per output row (b, h, q): merge the row's partials in chunk order.
-// Lane c holds chunk c's (m, l) (64 chunks per round), so the row max and
-// the weights f_c = 2^(m_c - M) take one round of loads and a wave
-// reduction; then every lane accumulates two dv columns over the chunks with
-// all of a round's loads in flight.  The merge order is fixed, so results
-// are bitwise reproducible.
+// One wave per output row (b, h, q): merge the row's partials in worker
+// order.  The pieces of group g were made by workers first..last of the same
+// partition (recomputed here) and sit at slots g + w.  Lane u of a round
+// holds one piece's (m, l), so the row max and the weights f = 2^(m - M) take
+// one round of loads and a wave reduction; then every lane accumulates two
+// dv columns over the pieces with a round of loads in flight.
 __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row_id = (int64_t)blockIdx.x * 4 + wave;
@@ -319,39 +429,46 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int b = (int)(row_id / ((int64_t)p.Q * p.Hq));
   const int kh = h / p.group;
   const int rr = (h - kh * p.group) * p.Q + qi;
-  const int Kb = clamp_len(p.seqlens, b, p.K);
-  int lo_u, hi_u;
-  group_key_range(Kb, p.Q, p.window, &lo_u, &hi_u);
-  const int c_lo = lo_u / p.chunk;
-  const int c_hi = hi_u > lo_u ? (hi_u + p.chunk - 1) / p.chunk : c_lo;
-  const int64_t split0 = ((int64_t)b * p.Hkv + kh) * p.n_splits;
   const int R = p.rows;
+  const int64_t g = (int64_t)b * p.Hkv + kh;
 
-  // Row max over the chunks (a chunk with no legal key for this row has m = -inf).
+  int w_first = 0, w_last = -1;
+  if (p.n_workers > 0 && p.K > 0) {
+    const SeqRange r = seq_range(p, b);
+    if (r.nsb > 0) {
+      const int64_t T = total_subblocks(p, lane);
+      const int64_t per = worker_share(T, p.n_workers);
+      const int64_t G = seq_base(p, b, lane) + (int64_t)kh * r.nsb;
+      w_first = (int)(G / per);
+      w_last = (int)((G + r.nsb - 1) / per);
+    }
+  }
+
+  // Row max over the pieces (a piece with no legal key for this row has m = -inf).
   float M = -INFINITY;
-  for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
-    const int cix = c0 + lane;
-    const float m = cix < c_hi ? p.ws_m[(split0 + cix) * R + rr] : -INFINITY;
+  for (int w0 = w_first; w0 <= w_last; w0 += 64) {
+    const int w = w0 + lane;
+    const float m = w <= w_last ? p.ws_m[(g + w) * R + rr] : -INFINITY;
     M = fmaxf(M, m);
   }
   M = wave_max(M);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
   if (M != -INFINITY) {
-    for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
-      const int cix = c0 + lane;
-      const int64_t sp = (split0 + cix) * R + rr;
-      const float m = cix < c_hi ? p.ws_m[sp] : -INFINITY;
+    for (int w0 = w_first; w0 <= w_last; w0 += 64) {
+      const int w = w0 + lane;
+      const int64_t sp = (g + w) * R + rr;
+      const float m = w <= w_last ? p.ws_m[sp] : -INFINITY;
       const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-      L += cix < c_hi ? p.ws_l[sp] * f : 0.f;
-      const int n = min(64, c_hi - c0);
-      // Lane `u` of the round holds f for chunk c0 + u.
+      L += w <= w_last ? p.ws_l[sp] * f : 0.f;
+      const int cnt = min(64, w_last + 1 - w0);
+      // Lane u of the round holds f for piece w0 + u.
       constexpr int U = 8;
-      for (int u0 = 0; u0 < n; u0 += U) {
+      for (int u0 = 0; u0 < cnt; u0 += U) {
         float a0[U], a1[U], fu[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const bool ok = u0 + u < n;
-          const float* a = p.ws_acc + ((split0 + c0 + u0 + u) * R + rr) * p.Dv;
+          const bool ok = u0 + u < cnt;
+          const float* a = p.ws_acc + ((g + w0 + u0 + u) * R + rr) * p.Dv;
           a0[u] = ok && lane < p.Dv ? a[lane] : 0.f;
           a1[u] = ok && lane + 64 < p.Dv ? a[lane + 64] : 0.f;
           fu[u] = __shfl(f, (u0 + u) & 63);
@@ -376,12 +493,10 @@ template <int DP, int DVP, int NT>
 static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   Params arg = p;
   void* args[] = {&arg};
-  // With K == 0 there is no split: the combine pass alone writes 0 / -inf.
-  if (p.n_splits > 0) {
-    const int64_t items = (int64_t)p.n_splits * p.Hkv * p.B;
-    const dim3 grid((unsigned)items);
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>), grid,
-                                         dim3(64), args, 0, stream);
+  // With K == 0 there is nothing to split: the combine pass alone writes 0 / -inf.
+  if (p.n_workers > 0) {
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>),
+                                         dim3((unsigned)p.n_workers), dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)p.B * p.Hq * p.Q;

@@ -86,15 +86,19 @@ const char* attn_fwd_strerror(int status);
 /*
  * The launch plan attn_fwd would use for these sizes, without launching
  * anything (host only).  path: 0 = no launch, 1 = prefill kernel,
- * 2 = split-KV decode + combine.  split_chunk is the keys per split (decode
- * path, else 0) and n_splits the splits per (batch, kv-head) at length K;
- * workspace_bytes the scratch the decode path takes from the pool.
- * Returns the status attn_fwd would return for an argument check.
+ * 2 = split-KV decode + combine.  On the decode path the keys of all
+ * (batch, kv-head) groups, in 32-key sub-blocks laid end to end, are cut
+ * into split_workers equal contiguous shares (0 when K == 0), each giving
+ * one partial softmax state per group piece; partial_slots bounds the
+ * pieces (B*Hkv + split_workers) and workspace_bytes is the scratch the
+ * decode path takes from the pool for them (partial_slots * g*Q rows *
+ * (Dv + 2) floats).  Returns the status attn_fwd would return for an
+ * argument check.
  */
 typedef struct attn_fwd_plan_t {
   int path;
-  int split_chunk;
-  int n_splits;
+  int split_workers;
+  int partial_slots;
   int64_t workspace_bytes;
 } attn_fwd_plan_t;
 

@@ -86,14 +86,17 @@ def test_slice_size_limit_boundary():
 def test_plan_selects_paths():
     assert af.attn_fwd_plan(4, 32, 8, 4096, 4096, 128, 128)["path"] == af.PATH_PREFILL
     p = af.attn_fwd_plan(64, 64, 8, 1, 32768, 128, 128)
-    assert p["path"] == af.PATH_DECODE and p["split_chunk"] % 128 == 0
-    assert p["n_splits"] == -(-32768 // p["split_chunk"])
-    assert p["workspace_bytes"] == 64 * 8 * p["n_splits"] * 8 * (128 + 2) * 4
+    assert p["path"] == af.PATH_DECODE and p["split_workers"] == 1024
+    assert p["partial_slots"] == 64 * 8 + 1024
+    assert p["workspace_bytes"] == p["partial_slots"] * 8 * (128 + 2) * 4
+    # Small problems: at least 4 sub-blocks of 32 keys per worker.
+    small = af.attn_fwd_plan(1, 8, 2, 1, 2053, 80, 96)
+    assert small["split_workers"] == -(-(2 * -(-2053 // 32)) // 4)
     assert af.attn_fwd_plan(1, 8, 2, 1, 2053, 80, 96)["path"] == af.PATH_DECODE
     assert af.attn_fwd_plan(1, 8, 2, 4, 100, 64, 64)["path"] == af.PATH_DECODE      # 16 packed rows
     assert af.attn_fwd_plan(1, 64, 1, 1, 100, 64, 64)["path"] == af.PATH_PREFILL    # 64 rows: prefill kernel
     assert af.attn_fwd_plan(1, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_PREFILL
     assert af.attn_fwd_plan(0, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_NONE
-    assert af.attn_fwd_plan(1, 8, 2, 1, 0, 64, 64)["n_splits"] == 0
+    assert af.attn_fwd_plan(1, 8, 2, 1, 0, 64, 64)["split_workers"] == 0
     with pytest.raises(af.AttnError):
         af.attn_fwd_plan(1, 8, 3, 1, 10, 64, 64)

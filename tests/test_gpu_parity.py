@@ -223,3 +223,21 @@ def test_running_max_moves(orc, pattern, Q):
     o, lse = run_gpu(w, q, k, v, scale=0.3)
     ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, scale=0.3)
     compare(o, lse, ro, rl, "bf16", f"running max {pattern}")
+
+
+@pytest.mark.parametrize("workers", [1, 2, 5, 13, 64, 4096])
+@pytest.mark.parametrize("Q,window", [(1, 0), (3, 0), (1, 50), (4, 97)])
+def test_decode_partitions(orc, workers, Q, window):
+    """The split pass cuts all groups' 32-key sub-blocks into `workers` equal
+    shares; pieces of a group then span worker boundaries in every way (tiny,
+    empty and long sequences, more workers than sub-blocks)."""
+    rng = np.random.default_rng(7)
+    sl = rng.integers(0, 700, size=24).astype(np.int32)
+    sl[[0, 5, 6]] = [0, 1, 2]
+    sl[[10, 11]] = [700, 33]
+    w = inputs.Workload("partitions", 24, 16, 4, Q, 700, 64, 64, seqlens=sl, window=window)
+    os.environ["ATTN_FWD_SPLIT_WORKERS"] = str(workers)
+    try:
+        _check(w, orc=orc, tag=f" workers={workers}")
+    finally:
+        del os.environ["ATTN_FWD_SPLIT_WORKERS"]
