@@ -415,10 +415,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 
 // One wave per output row (b, h, q): merge the row's partials in worker
 // order.  The pieces of group g were made by workers first..last of the same
-// partition (recomputed here) and sit at slots g + w.  Lane u of a round
-// holds one piece's (m, l), so the row max and the weights f = 2^(m - M) take
-// one round of loads and a wave reduction; then every lane accumulates two
-// dv columns over the pieces with a round of loads in flight.
+// partition (recomputed here) and sit at slots g + w.  Pieces are taken eight
+// at a time: every lane loads the eight pieces' (m, l) (the same addresses in
+// every lane) and its two dv columns of each, all in one round of loads, and
+// folds them into a running (M, L, o) that is rescaled when M moves, so a row
+// with at most eight pieces costs one round trip to memory.
 __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row_id = (int64_t)blockIdx.x * 4 + wave;
@@ -444,43 +445,39 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
     }
   }
 
-  // Row max over the pieces (a piece with no legal key for this row has m = -inf).
-  float M = -INFINITY;
-  for (int w0 = w_first; w0 <= w_last; w0 += 64) {
-    const int w = w0 + lane;
-    const float m = w <= w_last ? p.ws_m[(g + w) * R + rr] : -INFINITY;
-    M = fmaxf(M, m);
-  }
-  M = wave_max(M);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M != -INFINITY) {
-    for (int w0 = w_first; w0 <= w_last; w0 += 64) {
-      const int w = w0 + lane;
-      const int64_t sp = (g + w) * R + rr;
-      const float m = w <= w_last ? p.ws_m[sp] : -INFINITY;
-      const float f = m == -INFINITY ? 0.f : fast_exp2(m - M);
-      L += w <= w_last ? p.ws_l[sp] * f : 0.f;
-      const int cnt = min(64, w_last + 1 - w0);
-      // Lane u of the round holds f for piece w0 + u.
-      constexpr int U = 8;
-      for (int u0 = 0; u0 < cnt; u0 += U) {
-        float a0[U], a1[U], fu[U];
+  // Running merge; a piece with no legal key for this row has m = -inf and
+  // contributes nothing.
+  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+  constexpr int U = 8;
+  for (int w0 = w_first; w0 <= w_last; w0 += U) {
+    float m[U], l[U], a0[U], a1[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool ok = u0 + u < cnt;
-          const float* a = p.ws_acc + ((g + w0 + u0 + u) * R + rr) * p.Dv;
-          a0[u] = ok && lane < p.Dv ? a[lane] : 0.f;
-          a1[u] = ok && lane + 64 < p.Dv ? a[lane + 64] : 0.f;
-          fu[u] = __shfl(f, (u0 + u) & 63);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          o0 = fmaf(a0[u], fu[u], o0);
-          o1 = fmaf(a1[u], fu[u], o1);
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const bool ok = w0 + u <= w_last;
+      const int64_t sp = (g + w0 + u) * R + rr;
+      const float* a = p.ws_acc + sp * p.Dv;
+      m[u] = ok ? p.ws_m[sp] : -INFINITY;
+      l[u] = ok ? p.ws_l[sp] : 0.f;
+      a0[u] = ok && lane < p.Dv ? a[lane] : 0.f;
+      a1[u] = ok && lane + 64 < p.Dv ? a[lane + 64] : 0.f;
     }
-    L = wave_sum(L);
+    float mc = m[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mc = fmaxf(mc, m[u]);
+    if (mc == -INFINITY) continue;
+    const float mn = fmaxf(M, mc);
+    const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+    L *= alpha;
+    o0 *= alpha;
+    o1 *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float f = m[u] == -INFINITY ? 0.f : fast_exp2(m[u] - mn);
+      L = fmaf(l[u], f, L);
+      o0 = fmaf(a0[u], f, o0);
+      o1 = fmaf(a1[u], f, o1);
+    }
+    M = mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + row_id * p.Dv;
