@@ -85,7 +85,9 @@ def normal(shape, tensor_id: int, seed: int = SEED, dtype: str = "bf16", offset:
            threads: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
     """N(0,1) samples for elements [offset, offset+prod(shape)) of stream (seed, tensor_id).
 
-    dtype "bf16" returns the uint16 bit patterns; "f32" returns float32.
+    dtype "bf16" returns the uint16 bit patterns; "f32" returns float32; "f16"
+    returns float16, the float32 stream rounded to nearest even (numpy's
+    conversion).
     """
     n = int(np.prod(shape)) if len(shape) else 1
     lib = _load()
@@ -97,8 +99,14 @@ def normal(shape, tensor_id: int, seed: int = SEED, dtype: str = "bf16", offset:
         arr = out if out is not None else np.empty(shape, dtype=np.float32)
         assert arr.dtype == np.float32 and arr.size == n and arr.flags.c_contiguous
         lib.attn_inputs_normal_f32(arr.ctypes.data, n, offset, seed, tensor_id, threads or host_threads())
+    elif dtype == "f16":
+        tmp = np.empty(shape, dtype=np.float32)
+        lib.attn_inputs_normal_f32(tmp.ctypes.data, n, offset, seed, tensor_id, threads or host_threads())
+        arr = out if out is not None else np.empty(shape, dtype=np.float16)
+        assert arr.dtype == np.float16 and arr.size == n and arr.flags.c_contiguous
+        arr[...] = tmp.astype(np.float16)
     else:
-        raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+        raise ValueError(f"dtype must be 'bf16', 'f16' or 'f32', got {dtype!r}")
     return arr
 
 
@@ -140,12 +148,13 @@ class Workload:
     K: int
     D: int
     Dv: int
-    dtype: str = "bf16"          # "bf16" (bf16 in, bf16 O) or "f32"
+    dtype: str = "bf16"          # "bf16" (bf16 in, bf16 O), "f16" (fp16 in, fp16 O) or "f32"
     window: int = 0              # <= 0: no sliding window
     seqlens: Optional[np.ndarray] = None   # int32[B] or None (every K_b = K)
     seed: int = SEED
     note: str = ""
     scale: Optional[float] = None
+    causal: bool = True          # False: every key k < K_b is legal for every row (no window)
 
     def __post_init__(self):
         if self.scale is None:
@@ -175,6 +184,9 @@ class Workload:
         total = 0
         for b in range(self.B):
             Kb = self.kb(b)
+            if not self.causal:
+                total += self.Q * Kb
+                continue
             for q in range(self.Q):
                 p = q + Kb - self.Q
                 hi = min(Kb - 1, p)
@@ -205,7 +217,7 @@ class Workload:
             return normal(shape, tid, self.seed, self.dtype, threads=threads)
         if padding != "zero":
             raise ValueError(f"padding must be 'normal' or 'zero', got {padding!r}")
-        arr = np.zeros(shape, dtype=np.uint16 if self.dtype == "bf16" else np.float32)
+        arr = np.zeros(shape, dtype={"bf16": np.uint16, "f16": np.float16, "f32": np.float32}[self.dtype])
         B, H, T, W = shape
         for b in range(B):
             kb = self.kb(b)

@@ -8,7 +8,11 @@
  *
  * What is computed (LuisaCompute "Attention execution mapping" review,
  * section 1, the attention fixture paragraph): bottom-right causal
- * grouped-query attention.  Query head h reads kv-head h / (Hq/Hkv) (integer
+ * grouped-query attention, or, with causal = 0, the same attention without
+ * the causal limit: every key k < K_b is legal for every row (section 7 of
+ * the review names non-causal masks as an extension that needs its own
+ * semantics and an independent oracle; this is that semantics, written as
+ * plainly as the causal one).  Query head h reads kv-head h / (Hq/Hkv) (integer
  * division, contiguous groups); key k is legal for query row q when
  * k <= q + K - Q.  Readings where the pages are silent (each listed in the
  * design notes):
@@ -22,8 +26,12 @@
  * their sum, the normalised weights and the weighted sum of V rows.  There is
  * no blocking and no online rescaling.
  *
- * Inputs are read element by element from bf16 (dtype 0, widened exactly) or
- * fp32 (dtype 1) storage and every operation is done in double.  Row strides
+ * Inputs are read element by element from bf16 (dtype 0, widened exactly),
+ * fp32 (dtype 1) or IEEE binary16 (dtype 2, decoded exactly from its sign,
+ * 5-bit exponent and 10-bit fraction; the Laya "Fast backends" page,
+ * "Numerics", rounds GPU inputs to bf16 or fp16) storage and every operation
+ * is done in double.  A window needs the causal limit (it is measured back from the
+ * diagonal); causal = 0 with a window is rejected.  Row strides
  * (ldq, ldk, ldv, ldo) are in elements, so tests can embed V and O in wider
  * rows and check that columns beyond Dv are never read or written.
  *
@@ -39,6 +47,25 @@
 #define ORACLE_MUTANT 0
 #endif
 
+/* IEEE 754 binary16: value = (-1)^s * 2^(e-15) * (1 + f/1024) for 0 < e < 31,
+ * (-1)^s * 2^-14 * (f/1024) for e = 0, +-inf / NaN for e = 31. */
+static double half_to_double(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+  double mag;
+#if ORACLE_MUTANT == 15 /* exponent bias off by one */
+  const int bias = 16;
+#else
+  const int bias = 15;
+#endif
+  if (e == 0)
+    mag = ldexp((double)f, -24);
+  else if (e == 31)
+    mag = f ? NAN : INFINITY;
+  else
+    mag = ldexp(1.0 + (double)f / 1024.0, e - bias);
+  return s ? -mag : mag;
+}
+
 static double load_elem(const void* base, int dtype, int64_t i) {
   if (dtype == 0) {
     uint16_t h = ((const uint16_t*)base)[i];
@@ -47,15 +74,19 @@ static double load_elem(const void* base, int dtype, int64_t i) {
     memcpy(&f, &u, 4);
     return (double)f;
   }
+  if (dtype == 2) return half_to_double(((const uint16_t*)base)[i]);
   return (double)((const float*)base)[i];
 }
 
 /* The legality predicate of one (row, key) pair. */
-static int legal(int64_t k, int64_t p, int64_t Kb, int window) {
+static int legal(int64_t k, int64_t p, int64_t Kb, int window, int causal) {
+#if ORACLE_MUTANT == 14 /* causal limit applied to non-causal rows too */
+  causal = 1;
+#endif
 #if ORACLE_MUTANT == 3 /* causal diagonal off by one */
-  if (!(k <= p + 1)) return 0;
+  if (causal && !(k <= p + 1)) return 0;
 #else
-  if (!(k <= p)) return 0;
+  if (causal && !(k <= p)) return 0;
 #endif
   if (!(k >= 0 && k < Kb)) return 0;
 #if ORACLE_MUTANT == 5 /* window one key too wide */
@@ -71,8 +102,8 @@ static int legal(int64_t k, int64_t p, int64_t Kb, int window) {
  * legal keys, is_legal[k] marks them.  Returns the number of legal keys.
  */
 static int64_t row_scores(const void* q, const void* k, int dtype, int Hq, int Hkv, int Q, int K, int D,
-                          const int32_t* seqlens, int window, double scale, int64_t ldq, int64_t ldk, int b, int h,
-                          int qi, double* scores, unsigned char* is_legal) {
+                          const int32_t* seqlens, int window, int causal, double scale, int64_t ldq, int64_t ldk,
+                          int b, int h, int qi, double* scores, unsigned char* is_legal) {
 #if ORACLE_MUTANT == 2 /* wrong GQA map: modulo instead of integer division */
   int kh = h % Hkv;
 #else
@@ -92,7 +123,7 @@ static int64_t row_scores(const void* q, const void* k, int dtype, int Hq, int H
   const int64_t kbase = ((int64_t)b * Hkv + kh) * (int64_t)K;
   int64_t n_legal = 0;
   for (int64_t kk = 0; kk < K; ++kk) {
-    is_legal[kk] = (unsigned char)legal(kk, p, Kb, window);
+    is_legal[kk] = (unsigned char)legal(kk, p, Kb, window, causal);
     if (!is_legal[kk]) continue;
     ++n_legal;
     double dot = 0.0;
@@ -115,11 +146,11 @@ static int64_t row_scores(const void* q, const void* k, int dtype, int Hq, int H
 
 /* One output row (b, h, q): writes o_row[0..Dv) and *lse_out. */
 static void oracle_row(const void* q, const void* k, const void* v, int dtype, int Hq, int Hkv, int Q, int K,
-                       int D, int Dv, const int32_t* seqlens, int window, double scale, int64_t ldq, int64_t ldk,
-                       int64_t ldv, int b, int h, int qi, double* o_row, double* lse_out, double* scores,
-                       unsigned char* is_legal) {
-  int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, scale, ldq, ldk, b, h, qi, scores,
-                               is_legal);
+                       int D, int Dv, const int32_t* seqlens, int window, int causal, double scale, int64_t ldq,
+                       int64_t ldk, int64_t ldv, int b, int h, int qi, double* o_row, double* lse_out,
+                       double* scores, unsigned char* is_legal) {
+  int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, causal, scale, ldq, ldk, b, h, qi,
+                               scores, is_legal);
   if (n_legal == 0) {
     for (int j = 0; j < Dv; ++j) o_row[j] = 0.0;
     *lse_out = -INFINITY;
@@ -159,8 +190,11 @@ static void oracle_row(const void* q, const void* k, const void* v, int dtype, i
 #endif
 }
 
-static int check_args(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens) {
+static int check_args(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window,
+                      int causal, int dtype) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return -1;
+  if (dtype < 0 || dtype > 2) return -1;
+  if (!causal && window > 0) return -1;
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return -1;
   if (seqlens)
     for (int b = 0; b < B; ++b)
@@ -174,8 +208,8 @@ static int check_args(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const
  */
 int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, double* o, double* lse, int B, int Hq,
                     int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window, double scale,
-                    int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int threads) {
-  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens);
+                    int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, int threads, int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, dtype);
   if (rc) return rc;
   const int64_t rows = (int64_t)B * Hq * Q;
   int bad = 0;
@@ -194,7 +228,7 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, doub
       int qi = (int)(r % Q);
       int h = (int)((r / Q) % Hq);
       int b = (int)(r / ((int64_t)Q * Hq));
-      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, scale, ldq, ldk, ldv, b, h, qi,
+      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, scale, ldq, ldk, ldv, b, h, qi,
                  o + r * ldo, lse + r, scores, lg);
     }
     free(scores);
@@ -210,8 +244,8 @@ int oracle_attn_fwd(const void* q, const void* k, const void* v, int dtype, doub
  */
 int oracle_attn_fwd_rows(const void* q, const void* k, const void* v, int dtype, double* o, double* lse, int B,
                          int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window,
-                         double scale, const int64_t* rows, int64_t nrows, int threads) {
-  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens);
+                         double scale, const int64_t* rows, int64_t nrows, int threads, int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, dtype);
   if (rc) return rc;
   const int64_t total = (int64_t)B * Hq * Q;
   for (int64_t i = 0; i < nrows; ++i)
@@ -232,7 +266,7 @@ int oracle_attn_fwd_rows(const void* q, const void* k, const void* v, int dtype,
       int qi = (int)(r % Q);
       int h = (int)((r / Q) % Hq);
       int b = (int)(r / ((int64_t)Q * Hq));
-      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, scale, D, D, Dv, b, h, qi,
+      oracle_row(q, k, v, dtype, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, scale, D, D, Dv, b, h, qi,
                  o + i * Dv, lse + i, scores, lg);
     }
     free(scores);
@@ -247,8 +281,9 @@ int oracle_attn_fwd_rows(const void* q, const void* k, const void* v, int dtype,
  * or a negative code as oracle_attn_fwd does.
  */
 int64_t oracle_attn_probs(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int Q, int K, int D,
-                          const int32_t* seqlens, int window, double scale, int b, int h, int qi, double* p_out) {
-  int rc = check_args(B, Hq, Hkv, Q, K, D, 1, seqlens);
+                          const int32_t* seqlens, int window, double scale, int b, int h, int qi, double* p_out,
+                          int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, 1, seqlens, window, causal, dtype);
   if (rc) return rc;
   double* scores = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
   unsigned char* lg = (unsigned char*)malloc((size_t)(K > 0 ? K : 1));
@@ -257,7 +292,8 @@ int64_t oracle_attn_probs(const void* q, const void* k, int dtype, int B, int Hq
     free(lg);
     return -3;
   }
-  int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, scale, D, D, b, h, qi, scores, lg);
+  int64_t n_legal =
+      row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, causal, scale, D, D, b, h, qi, scores, lg);
   double m = -INFINITY;
   for (int64_t kk = 0; kk < K; ++kk)
     if (lg[kk] && scores[kk] > m) m = scores[kk];

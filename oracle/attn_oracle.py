@@ -4,8 +4,9 @@ Follows the attention fixture of the LuisaCompute "Attention execution
 mapping" review (section 1): bottom-right causal GQA, kv-head h/(Hq/Hkv),
 legal keys k <= q + K_b - Q (K_b replaces K for per-sequence lengths), an
 optional window of W keys ending at the diagonal, O = 0 / LSE = -inf for rows
-without a legal key.  Inputs are host arrays: bf16 as uint16 bit patterns
-(dtype "bf16") or float32 (dtype "f32").  Results are float64.
+without a legal key; with causal=False every key k < K_b is legal for every
+row (no window).  Inputs are host arrays: bf16 as uint16 bit patterns,
+float32, or IEEE binary16 (numpy float16).  Results are float64.
 """
 from __future__ import annotations
 
@@ -22,12 +23,12 @@ _libs: dict[str, ctypes.CDLL] = {}
 def _setup(lib):
     vp, ci, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_attn_fwd.argtypes = [vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl,
-                                    i64, i64, i64, i64, ci]
+                                    i64, i64, i64, i64, ci, ci]
     lib.oracle_attn_fwd.restype = ci
     lib.oracle_attn_fwd_rows.argtypes = [vp, vp, vp, ci, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl,
-                                         vp, i64, ci]
+                                         vp, i64, ci, ci]
     lib.oracle_attn_fwd_rows.restype = ci
-    lib.oracle_attn_probs.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci, ci, ci, vp]
+    lib.oracle_attn_probs.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci, ci, ci, vp, ci]
     lib.oracle_attn_probs.restype = i64
     return lib
 
@@ -46,7 +47,9 @@ def _dtype_code(arr: np.ndarray) -> int:
         return 0
     if arr.dtype == np.float32:
         return 1
-    raise TypeError("oracle inputs are bf16 bit patterns (uint16) or float32")
+    if arr.dtype == np.float16:
+        return 2
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16), float32 or float16")
 
 
 def _threads(threads: int) -> int:
@@ -66,7 +69,7 @@ class Oracle:
     def __init__(self, lib):
         self.lib = lib
 
-    def fwd(self, q, k, v, *, seqlens=None, window=0, scale=None, threads=0, ld=None):
+    def fwd(self, q, k, v, *, seqlens=None, window=0, scale=None, threads=0, ld=None, causal=True):
         """Full forward.  q [B,Hq,Q,*], k [B,Hkv,K,*], v [B,Hkv,K,*] (row strides taken
         from the last axis unless `ld` = (ldq, ldk, ldv, ldo, D, Dv) is given).
         Returns (o [B,Hq,Q,Dv] float64, lse [B,Hq,Q] float64)."""
@@ -91,12 +94,12 @@ class Oracle:
         rc = self.lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, code, o.ctypes.data,
                                       lse.ctypes.data, B, Hq, Hkv, Q, K, D, Dv,
                                       None if sl is None else sl.ctypes.data, int(window), float(scale),
-                                      ldq, ldk, ldv, ldo, _threads(threads))
+                                      ldq, ldk, ldv, ldo, _threads(threads), int(bool(causal)))
         if rc:
             raise OracleError(f"oracle_attn_fwd returned {rc}")
         return o, lse
 
-    def fwd_into(self, q, k, v, o, lse, *, D, Dv, seqlens=None, window=0, scale=None, threads=0):
+    def fwd_into(self, q, k, v, o, lse, *, D, Dv, seqlens=None, window=0, scale=None, threads=0, causal=True):
         """Like fwd but writes into caller-provided wide rows (o's last axis may exceed Dv)."""
         B, Hq, Q, ldq = q.shape
         _, Hkv, K, ldk = k.shape
@@ -109,11 +112,11 @@ class Oracle:
         rc = self.lib.oracle_attn_fwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, code, o.ctypes.data,
                                       lse.ctypes.data, B, Hq, Hkv, Q, K, D, Dv,
                                       None if sl is None else sl.ctypes.data, int(window), float(scale),
-                                      ldq, ldk, ldv, ldo, _threads(threads))
+                                      ldq, ldk, ldv, ldo, _threads(threads), int(bool(causal)))
         if rc:
             raise OracleError(f"oracle_attn_fwd returned {rc}")
 
-    def rows(self, q, k, v, rows, *, seqlens=None, window=0, scale=None, threads=0, shape=None):
+    def rows(self, q, k, v, rows, *, seqlens=None, window=0, scale=None, threads=0, shape=None, causal=True):
         """Selected flat rows (b*Hq+h)*Q+q.  q/k/v may be full arrays, or any buffers when
         `shape` = (B,Hq,Hkv,Q,K,D,Dv) is given.  Returns (o [n,Dv], lse [n])."""
         if shape is None:
@@ -132,12 +135,12 @@ class Oracle:
         rc = self.lib.oracle_attn_fwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, code, o.ctypes.data,
                                            lse.ctypes.data, B, Hq, Hkv, Q, K, D, Dv,
                                            None if sl is None else sl.ctypes.data, int(window), float(scale),
-                                           r.ctypes.data, len(r), _threads(threads))
+                                           r.ctypes.data, len(r), _threads(threads), int(bool(causal)))
         if rc:
             raise OracleError(f"oracle_attn_fwd_rows returned {rc}")
         return o, lse
 
-    def probs(self, q, k, b, h, qi, *, seqlens=None, window=0, scale=None):
+    def probs(self, q, k, b, h, qi, *, seqlens=None, window=0, scale=None, causal=True):
         """Normalised weights of one row over all K key slots (0 where not legal)."""
         B, Hq, Q, D = q.shape
         _, Hkv, K, _ = k.shape
@@ -147,7 +150,7 @@ class Oracle:
         sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
         n = self.lib.oracle_attn_probs(q.ctypes.data, k.ctypes.data, _dtype_code(q), B, Hq, Hkv, Q, K, D,
                                        None if sl is None else sl.ctypes.data, int(window), float(scale),
-                                       b, h, qi, p.ctypes.data)
+                                       b, h, qi, p.ctypes.data, int(bool(causal)))
         if n < 0:
             raise OracleError(f"oracle_attn_probs returned {n}")
         return p[:K], int(n)

@@ -5,7 +5,8 @@ whole [Q, K] boolean mask and score matrix for each (batch, head) and sums
 with math.fsum (correctly rounded).  It exists to cross-check the C oracle on
 small shapes; it follows the same definition (LuisaCompute "Attention
 execution mapping" review, section 1; per-sequence lengths and window as read
-in the design notes) but shares no code with it.
+in the design notes; causal=False drops the causal limit) but shares no code
+with it.
 """
 from __future__ import annotations
 
@@ -15,12 +16,13 @@ import numpy as np
 
 
 def widen(a: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16), float16 or float32 -> float64 (all exact)."""
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
 
 
-def attention(q, k, v, *, seqlens=None, window=0, scale=None):
+def attention(q, k, v, *, seqlens=None, window=0, scale=None, causal=True):
     qd, kd, vd = widen(q), widen(k), widen(v)
     B, Hq, Q, D = qd.shape
     _, Hkv, K, _ = kd.shape
@@ -34,7 +36,9 @@ def attention(q, k, v, *, seqlens=None, window=0, scale=None):
         Kb = K if seqlens is None else int(seqlens[b])
         qpos = np.arange(Q)[:, None] + Kb - Q          # absolute position of each query row
         kpos = np.arange(K)[None, :]
-        mask = (kpos <= qpos) & (kpos < Kb)
+        mask = (kpos < Kb) & np.ones((Q, 1), dtype=bool)
+        if causal:
+            mask &= kpos <= qpos
         if window > 0:
             mask &= kpos > qpos - window
         for h in range(Hq):

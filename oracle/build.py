@@ -27,6 +27,8 @@ MUTANTS = {
     11: "last channel of the dot product dropped",
     12: "score sign flipped",
     13: "LSE in base 2",
+    14: "causal limit kept for non-causal rows",
+    15: "fp16 exponent bias off by one",
 }
 
 

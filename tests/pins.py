@@ -6,6 +6,9 @@ AssertionError when the oracle disagrees with:
   - textbook causal attention as computed by torch's scaled_dot_product_attention
     in float64 on the CPU (a library routine),
   - closed forms (uniform V, a single legal key, zero scale),
+  - numpy's float16 conversion (every finite binary16 pattern),
+  - torch's unmasked attention for the non-causal mode, and key-order
+    independence there,
   - invariants (shift of K along a fixed direction, weights summing to one,
     split-and-merge by log-sum-exp, GQA equal to MHA on repeated heads,
     padding never read, V/O columns beyond Dv never touched).
@@ -285,6 +288,110 @@ def pin_v_columns_untouched(orc):
     _close(ow[..., :Dv], o_ref, 0.0, "wide-row O equals narrow-row O")
 
 
+# ---------------------------------------------------------------- fp16 storage
+def pin_fp16_decode(orc):
+    """Every finite IEEE binary16 pattern is read as its exact value: batch b is a
+    one-row, one-key problem with q = pattern b, k = 1.0 and scale 1, so its LSE is
+    q itself; numpy's float16 -> float64 conversion is the reference."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    bits = bits[np.isfinite(vals)]
+    n = len(bits)
+    q = bits.view(np.float16).reshape(n, 1, 1, 1).copy()
+    k = np.ones((n, 1, 1, 1), dtype=np.float16)
+    v = np.ones((n, 1, 1, 1), dtype=np.float16)
+    o, lse = orc.fwd(q, k, v, scale=1.0)
+    want = q.astype(np.float64).reshape(n, 1, 1)
+    assert np.array_equal(lse, want), "fp16 inputs must decode exactly"
+    assert np.all(o == 1.0)
+
+
+# ---------------------------------------------------------------- non-causal
+def _sdpa_full(q, k, v, scale, kb=None):
+    """Attention without a mask via torch (float64, CPU), kv heads repeated over their
+    query groups; kb limits every batch entry to its first kb[b] keys."""
+    B = q.shape[0]
+    g = q.shape[1] // k.shape[1]
+    outs, lses = [], []
+    for b in range(B):
+        n = k.shape[2] if kb is None else int(kb[b])
+        tq = torch.from_numpy(q[b:b + 1].astype(np.float64))
+        if n == 0:
+            outs.append(np.zeros(q[b:b + 1].shape[:3] + (v.shape[-1],)))
+            lses.append(np.full(q[b:b + 1].shape[:3], -np.inf))
+            continue
+        tk = torch.from_numpy(k[b:b + 1, :, :n].astype(np.float64)).repeat_interleave(g, dim=1)
+        tv = torch.from_numpy(v[b:b + 1, :, :n].astype(np.float64)).repeat_interleave(g, dim=1)
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=False, scale=scale)
+        s = scale * torch.matmul(tq, tk.transpose(-1, -2).contiguous())
+        outs.append(o.numpy())
+        lses.append(torch.logsumexp(s, dim=-1).numpy())
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def pin_noncausal_textbook(orc):
+    """causal=False is plain (unmasked) attention over each entry's first K_b keys."""
+    rng = np.random.default_rng(24)
+    for (B, Hq, Hkv, Q, K, D, Dv, sl) in [(2, 4, 2, 7, 19, 16, 8, None), (1, 3, 1, 21, 5, 8, 12, None),
+                                          (3, 4, 2, 1, 13, 16, 16, [13, 0, 4]), (2, 2, 2, 9, 9, 7, 5, [3, 9])]:
+        q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+        scale = 0.3
+        sla = None if sl is None else np.array(sl, np.int32)
+        o, lse = orc.fwd(q, k, v, seqlens=sla, scale=scale, causal=False)
+        ro, rl = _sdpa_full(q, k, v, scale, sla)
+        _close(o, ro, 1e-12, f"non-causal O {B,Hq,Hkv,Q,K,D,Dv,sl}")
+        _close(lse, rl, 1e-12, f"non-causal LSE {B,Hq,Hkv,Q,K,D,Dv,sl}")
+
+
+def pin_noncausal_key_order(orc):
+    """Without the causal limit the keys form a set: permuting the first K_b rows of K
+    and V together changes nothing (with the limit it would)."""
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 4, 2, 6, 17, 16, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    sl = np.array([17, 11], np.int32)
+    o1, l1 = orc.fwd(q, k, v, seqlens=sl, causal=False)
+    k2, v2 = k.copy(), v.copy()
+    for b in range(B):
+        perm = rng.permutation(int(sl[b]))
+        k2[b, :, :sl[b]] = k[b][:, perm]
+        v2[b, :, :sl[b]] = v[b][:, perm]
+    o2, l2 = orc.fwd(q, k2, v2, seqlens=sl, causal=False)
+    _close(o2, o1, 1e-12, "non-causal key permutation O")
+    _close(l2, l1, 1e-12, "non-causal key permutation LSE")
+
+
+def pin_noncausal_closed_forms(orc):
+    """causal=False, scale 0: O is the mean of the first K_b V rows, LSE ln K_b (every
+    row, whatever its position); K_b = 0 rows give O = 0, LSE = -inf."""
+    rng = np.random.default_rng(26)
+    B, Hq, Hkv, Q, K, D, Dv = 3, 2, 1, 5, 9, 8, 6
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    sl = np.array([9, 2, 0], np.int32)
+    o, lse = orc.fwd(q, k, v, seqlens=sl, scale=0.0, causal=False)
+    vd = v.astype(np.float64)
+    for b in range(B):
+        n = int(sl[b])
+        for h in range(Hq):
+            for i in range(Q):
+                if n == 0:
+                    assert np.all(o[b, h, i] == 0.0) and np.isneginf(lse[b, h, i]), "K_b = 0 row"
+                else:
+                    _close(o[b, h, i], vd[b, 0, :n].mean(axis=0), 1e-12, "non-causal scale 0 O")
+                    _close(lse[b, h, i], math.log(n), 1e-12, "non-causal scale 0 LSE")
+
+
+def pin_noncausal_needs_no_window(orc):
+    """A window is measured back from the diagonal, so it needs the causal limit."""
+    q = np.zeros((1, 1, 1, 8), np.float32)
+    try:
+        orc.fwd(q, q, q, window=4, causal=False)
+    except Exception as e:  # OracleError
+        assert "returned -1" in str(e)
+        return
+    raise AssertionError("causal=False with a window must be rejected")
+
+
 # ---------------------------------------------------------------- second implementation
 BRUTE_SHAPES = [
     # B,Hq,Hkv,Q,K,D,Dv, window, seqlens
@@ -294,6 +401,13 @@ BRUTE_SHAPES = [
     (1, 2, 1, 3, 67, 33, 7, 4, None),
     (3, 4, 4, 4, 12, 16, 8, 3, [0, 12, 5]),
     (2, 8, 2, 1, 33, 16, 24, 0, [33, 1]),      # decode, MQA-like groups
+]
+# Non-causal and fp16-storage cases: B,Hq,Hkv,Q,K,D,Dv, seqlens, storage
+BRUTE_EXTRA = [
+    (1, 4, 2, 9, 5, 8, 8, None, "f32", False),
+    (3, 4, 4, 4, 12, 16, 8, [0, 12, 5], "f32", False),
+    (2, 4, 2, 6, 21, 16, 24, [21, 7], "f16", True),
+    (1, 2, 1, 3, 35, 8, 8, None, "f16", False),
 ]
 
 
@@ -306,11 +420,20 @@ def pin_brute_force(orc):
         bo, bl = brute.attention(q, k, v, seqlens=sla, window=W)
         _close(o, bo, 1e-12, f"brute force O {B,Hq,Hkv,Q,K,D,Dv,W,sl}")
         _close(lse, bl, 1e-12, f"brute force LSE {B,Hq,Hkv,Q,K,D,Dv,W,sl}")
+    for (B, Hq, Hkv, Q, K, D, Dv, sl, st, causal) in BRUTE_EXTRA:
+        mk = (lambda shape: _f32(rng, shape).astype(np.float16)) if st == "f16" else (lambda shape: _f32(rng, shape))
+        q, k, v = mk((B, Hq, Q, D)), mk((B, Hkv, K, D)), mk((B, Hkv, K, Dv))
+        sla = None if sl is None else np.array(sl, np.int32)
+        o, lse = orc.fwd(q, k, v, seqlens=sla, causal=causal)
+        bo, bl = brute.attention(q, k, v, seqlens=sla, causal=causal)
+        _close(o, bo, 1e-12, f"brute force O {B,Hq,Hkv,Q,K,D,Dv,sl,st,causal}")
+        _close(lse, bl, 1e-12, f"brute force LSE {B,Hq,Hkv,Q,K,D,Dv,sl,st,causal}")
 
 
 INDEPENDENT_PINS = [
     pin_worked_examples, pin_textbook_causal, pin_bottom_right, pin_uniform_v, pin_single_key,
     pin_scale_zero, pin_empty_rows, pin_shift_invariance, pin_probs_sum_to_one, pin_split_merge,
-    pin_gqa_expand, pin_varlen_unpadded, pin_v_columns_untouched,
+    pin_gqa_expand, pin_varlen_unpadded, pin_v_columns_untouched, pin_fp16_decode, pin_noncausal_textbook,
+    pin_noncausal_key_order, pin_noncausal_closed_forms, pin_noncausal_needs_no_window,
 ]
 ALL_PINS = INDEPENDENT_PINS + [pin_brute_force]

@@ -89,6 +89,23 @@ def test_bf16_stream_is_rounded_f32_stream():
     np.testing.assert_array_equal(inputs.f32_to_bf16_bits(f), b)
 
 
+def test_f16_stream_is_rounded_f32_stream():
+    f = inputs.normal((4099,), tensor_id=5, dtype="f32")
+    h = inputs.normal((4099,), tensor_id=5, dtype="f16")
+    assert h.dtype == np.float16
+    np.testing.assert_array_equal(f.astype(np.float16), h)
+    # round to nearest, ties to even: 1 + 2^-11 lies halfway between 1 and 1 + 2^-10
+    ties = np.array([1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11], dtype=np.float32)
+    np.testing.assert_array_equal(ties.astype(np.float16).astype(np.float64), [1.0, 1.0 + 2 * 2.0 ** -10])
+    part = inputs.normal((7,), tensor_id=5, dtype="f16", offset=100)
+    np.testing.assert_array_equal(part, h[100:107])
+
+
+def test_noncausal_pair_count():
+    w = inputs.Workload("nc", 2, 4, 2, 5, 9, 16, 16, causal=False, seqlens=np.array([9, 3], np.int32))
+    assert w.legal_pairs() == 4 * 5 * (9 + 3)
+
+
 def test_config_recipes():
     c1 = inputs.config(1)
     assert c1.shape_tuple == (1, 4, 2, 64, 128, 64, 64) and c1.dtype == "f32" and c1.seqlens is None
