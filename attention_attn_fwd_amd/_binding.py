@@ -17,9 +17,11 @@ LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_OOM, ATTN_ERR_HIP = range(5)
 PATH_NONE, PATH_PREFILL, PATH_DECODE = 0, 1, 2
+# attn_fwd_ex flags
+ATTN_FWD_FP16, ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL = 1, 2, 4
 
 # Every function the header declares; a CPU test checks the library exports all of them.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_strerror", "attn_fwd_plan")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_strerror", "attn_fwd_plan")
 
 
 class AttnError(RuntimeError):
@@ -50,6 +52,8 @@ def load():
         lib.attn_fwd.restype = ci
         lib.attn_fwd_f32.argtypes = sig
         lib.attn_fwd_f32.restype = ci
+        lib.attn_fwd_ex.argtypes = sig[:-1] + [ci, vp]
+        lib.attn_fwd_ex.restype = ci
         lib.attn_fwd_strerror.argtypes = [ci]
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Plan)]
@@ -93,6 +97,12 @@ def attn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, sc
                                _ptr(seqlens_k), int(window), float(scale), _stream(stream))
 
 
+def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags, stream) -> int:
+    """Raw C call with option flags (ATTN_FWD_FP16 / _FP32 / _NONCAUSAL); returns the status."""
+    return load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
+                              _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
+
+
 def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
     plan = _Plan()
     st = load().attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, int(window), ctypes.byref(plan))
@@ -103,18 +113,19 @@ def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
 
 
 def forward(q, k, v, seqlens_k=None, window: int = 0, scale: Optional[float] = None, out=None, lse=None,
-            stream=None):
-    """Causal GQA attention forward on torch tensors.
+            stream=None, causal: bool = True):
+    """GQA attention forward on torch tensors (causal unless causal=False).
 
     q [B,Hq,Q,D], k [B,Hkv,K,D], v [B,Hkv,K,Dv]: contiguous, on the GPU, all
-    bfloat16 (bf16 kernels, bf16 output) or all float32 (fp32 kernel).
-    seqlens_k: int32 [B] on the same device, or None.  Returns (o, lse) with
-    o [B,Hq,Q,Dv] in the input dtype and lse [B,Hq,Q] float32.
+    bfloat16 or all float16 (MFMA kernels, output in the input type) or all
+    float32 (fp32 kernel).  seqlens_k: int32 [B] on the same device, or None.
+    Returns (o, lse) with o [B,Hq,Q,Dv] in the input dtype and lse [B,Hq,Q]
+    float32.
     """
     import torch
 
-    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q, k, v must all be bfloat16 or all float32")
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise TypeError("q, k, v must all be bfloat16, all float16 or all float32")
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")
@@ -139,8 +150,10 @@ def forward(q, k, v, seqlens_k=None, window: int = 0, scale: Optional[float] = N
         lse = torch.empty((B, Hq, Q), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fn = attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32
-    st = fn(q, k, v, out, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream)
+    flags = {torch.bfloat16: 0, torch.float16: ATTN_FWD_FP16, torch.float32: ATTN_FWD_FP32}[q.dtype]
+    if not causal:
+        flags |= ATTN_FWD_NONCAUSAL
+    st = attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags, stream)
     if st != ATTN_OK:
-        raise AttnError(st, fn.__name__)
+        raise AttnError(st, "attn_fwd_ex")
     return out, lse

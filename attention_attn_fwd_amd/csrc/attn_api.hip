@@ -110,8 +110,16 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   return ATTN_OK;
 }
 
-int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
+// flags: ATTN_FWD_FP16 / ATTN_FWD_FP32 select the element type (bf16 when
+// neither), ATTN_FWD_NONCAUSAL drops the causal limit.
+int run(int flags, const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
         int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream_) {
+  constexpr int kKnown = ATTN_FWD_FP16 | ATTN_FWD_FP32 | ATTN_FWD_NONCAUSAL;
+  if ((flags & ~kKnown) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((flags & ATTN_FWD_FP16) && (flags & ATTN_FWD_FP32)) return ATTN_ERR_INVALID_ARG;
+  const bool causal = !(flags & ATTN_FWD_NONCAUSAL);
+  if (!causal && window > 0) return ATTN_ERR_INVALID_ARG;
+  const bool bf16 = !(flags & ATTN_FWD_FP32);  // a 16-bit type: the MFMA kernels
   attn_fwd_plan_t plan;
   int st = check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, scale, bf16, &plan);
   if (st != ATTN_OK || plan.path == 0) return st;
@@ -125,6 +133,8 @@ int run(bool bf16, const void* q, const void* k, const void* v, void* o, float* 
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse; p.seqlens = seqlens_k;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Q = Q; p.K = K; p.D = D; p.Dv = Dv;
   p.window = window > 0 ? window : 0;
+  p.causal_shift = causal ? 0 : kNonCausalShift;
+  p.f16 = (flags & ATTN_FWD_FP16) ? 1 : 0;
   p.group = Hq / Hkv;
   p.q_sign = scale < 0.f ? 1 : 0;
   // Kept strictly positive so a masked score (-inf) times it stays -inf; a
@@ -170,12 +180,17 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q, int K,
              int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream) {
-  return attn::run(true, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+  return attn::run(0, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int Q,
                  int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream) {
-  return attn::run(false, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+  return attn::run(ATTN_FWD_FP32, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
+                int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream) {
+  return attn::run(flags, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
 }
 
 const char* attn_fwd_strerror(int status) {

@@ -39,6 +39,8 @@ struct Params {
   const int32_t* seqlens;  // may be null: every K_b = K
   int B, Hq, Hkv, Q, K, D, Dv;
   int window;              // <= 0: none
+  int causal_shift;        // 0, or kNonCausalShift: no causal limit (see row_delta)
+  int f16;                 // bf16 kernels: 1 when q, k, v, o are IEEE binary16 instead of bf16
   int group;               // Hq / Hkv
   int q_sign;              // 0x8000 when the scale is negative (q is negated), else 0
   float scale_log2;        // |scale| * log2(e)
@@ -58,6 +60,14 @@ hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
 
 // Padded widths the kernels are instantiated for.
 inline int pad_width(int d) { return d <= 64 ? 64 : 128; }
+
+// Row q of sequence b sits at absolute position q + row_delta: K_b - Q
+// (bottom-right alignment), or, without the causal limit, far enough past
+// every key that the causal test k <= position never excludes one.  With the
+// shift, positions stay below 2^31 for every size the library accepts
+// (Q, K < 2^27).
+constexpr int kNonCausalShift = 1 << 30;
+__host__ __device__ inline int row_delta(int Kb, int Q, int causal_shift) { return Kb - Q + causal_shift; }
 
 // ---------------------------------------------------------------------------
 // Device building blocks
@@ -186,6 +196,34 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
   r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
   return r;
 }
+
+// The 16-bit element type of the matrix kernels: bf16 (F16 = false) or IEEE
+// binary16 (F16 = true).  Fragments travel as bf16x8 bit patterns (loads and
+// LDS reads only move bits); the MFMA, the packing of the softmax weights and
+// the output conversion are the type's own.
+template <bool F16>
+struct Elem;
+template <>
+struct Elem<false> {
+  __device__ static f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16x16x32(a, b, c); }
+  __device__ static bf16x8 pack(f32x4 lo, f32x4 hi) { return pack_bf16x8(lo, hi); }
+  __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+};
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <>
+struct Elem<true> {
+  __device__ static f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  }
+  __device__ static bf16x8 pack(f32x4 lo, f32x4 hi) {
+    f16x8 r;
+    r[0] = (_Float16)lo[0]; r[1] = (_Float16)lo[1]; r[2] = (_Float16)lo[2]; r[3] = (_Float16)lo[3];
+    r[4] = (_Float16)hi[0]; r[5] = (_Float16)hi[1]; r[6] = (_Float16)hi[2]; r[7] = (_Float16)hi[3];
+    return __builtin_bit_cast(bf16x8, r);
+  }
+  __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
 
 __device__ __forceinline__ bf16x8 concat_bf16x4(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);

@@ -131,9 +131,10 @@ __device__ __forceinline__ void make_uniform(Cursor& c) {
   c.Kb = __builtin_amdgcn_readfirstlane(c.Kb);
 }
 
-template <int DP, int DVP, int NT>
+template <int DP, int DVP, int NT, bool F16>
 __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   using S = DecodeShape<DP, DVP, NT>;
+  using E = Elem<F16>;
   __shared__ __attribute__((aligned(16))) unsigned char ring[2 * S::STAGE];
 
   const int lane = threadIdx.x;
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     const unsigned char* kst = ring + stg * S::STAGE;
     const unsigned char* vst = kst + S::K_STAGE;
     const bool opens = stage_q[stg];  // first sub-block of a group in this share
-    const int Kb = cc.Kb, delta = Kb - Qn;
+    const int Kb = cc.Kb, delta = row_delta(Kb, Qn, p.causal_shift);
     const int kb0 = cc.lo + cc.sb * kDecodeSub;
 
     if (opens) {
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sacc[i][t] = mfma16x16x32(kf[i][s], qf[t][s], sacc[i][t]);
+        for (int t = 0; t < NT; ++t) sacc[i][t] = E::mfma(kf[i][s], qf[t][s], sacc[i][t]);
     // Every row sees keys <= K_b - Q causally; the last row's window starts at K_b - W.
     const bool full = (kb0 + kDecodeSub - 1 <= delta) && (kb0 + kDecodeSub <= Kb) && (W <= 0 || kb0 >= Kb - W);
     if (!full) {
@@ -370,13 +371,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
         }
       }
       l_run[t] += rs;
-      pf[t] = pack_bf16x8(sacc[0][t], sacc[1][t]);
+      pf[t] = E::pack(sacc[0][t], sacc[1][t]);
     }
     // O^T += V^T P^T.
 #pragma unroll
     for (int jv = 0; jv < S::JV; ++jv)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[jv][t] = mfma16x16x32(vf[jv], pf[t], acc[jv][t]);
+      for (int t = 0; t < NT; ++t) acc[jv][t] = E::mfma(vf[jv], pf[t], acc[jv][t]);
 
     // The stage is free once its LDS reads have returned: refill it with
     // sub-block j + 2.
@@ -481,8 +482,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + row_id * p.Dv;
-  if (lane < p.Dv) orow[lane] = __builtin_bit_cast(uint16_t, (__bf16)(o0 * inv));
-  if (lane + 64 < p.Dv) orow[lane + 64] = __builtin_bit_cast(uint16_t, (__bf16)(o1 * inv));
+  auto cvt = [&](float x) { return p.f16 ? Elem<true>::cvt(x) : Elem<false>::cvt(x); };
+  if (lane < p.Dv) orow[lane] = cvt(o0 * inv);
+  if (lane + 64 < p.Dv) orow[lane + 64] = cvt(o1 * inv);
   if (lane == 0) p.lse[row_id] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
 
@@ -492,8 +494,9 @@ static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   void* args[] = {&arg};
   // With K == 0 there is nothing to split: the combine pass alone writes 0 / -inf.
   if (p.n_workers > 0) {
-    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT>),
-                                         dim3((unsigned)p.n_workers), dim3(64), args, 0, stream);
+    const void* fn = p.f16 ? reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT, true>)
+                           : reinterpret_cast<const void*>(&decode_split_kernel<DP, DVP, NT, false>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.n_workers), dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
   }
   const int64_t rows = (int64_t)p.B * p.Hq * p.Q;

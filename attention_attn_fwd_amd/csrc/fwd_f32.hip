@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(Params p) {
   const int qt = n_qt - 1 - x;
   const int kh = h / p.group;
   const int Kb = clamp_len(p.seqlens, b, p.K);
-  const int delta = Kb - p.Q, W = p.window;
+  const int delta = row_delta(Kb, p.Q, p.causal_shift), W = p.window;
   const int q0 = qt * kF32Rows, q_end = min(q0 + kF32Rows, p.Q);
   const int kv_hi = min(Kb, q_end - 1 + delta + 1);
   const int kv_lo = W > 0 ? max(0, q0 + delta - W + 1) : 0;

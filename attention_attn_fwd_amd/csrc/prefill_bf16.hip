@@ -86,9 +86,11 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int n_qt, int* qt,
 
 // EXACT: D == DP and Dv == DVP, so row strides are compile-time constants and
 // no channel is padding (the common case); otherwise padded channels read zero.
-template <int DP, int DVP, bool EXACT>
+// F16: the 16-bit inputs and output are IEEE binary16 instead of bf16.
+template <int DP, int DVP, bool EXACT, bool F16>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   using S = PrefillShape<DP, DVP>;
+  using E = Elem<F16>;
   constexpr int BN = kPrefillBN;
   const int D = EXACT ? DP : p.D;
   const int Dv = EXACT ? DVP : p.Dv;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int kh = h / p.group;
 
   const int Kb = clamp_len(p.seqlens, b, p.K);
-  const int delta = Kb - p.Q;  // absolute position of row q is q + delta
+  const int delta = row_delta(Kb, p.Q, p.causal_shift);  // absolute position of row q is q + delta
   const int W = p.window;
   const int q0 = qt * kPrefillBM;
   const int q_end = min(q0 + kPrefillBM, p.Q);
@@ -297,8 +299,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       l_run[t] += rs[t];
-      pf[t][0] = pack_bf16x8(e[0][t], e[1][t]);
-      pf[t][1] = pack_bf16x8(e[2][t], e[3][t]);
+      pf[t][0] = E::pack(e[0][t], e[1][t]);
+      pf[t][1] = E::pack(e[2][t], e[3][t]);
     }
   };
 
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
-              s[i][t] = mfma16x16x32(ak[st & 1][i], qf[t][st], c0);
+              s[i][t] = E::mfma(ak[st & 1][i], qf[t][st], c0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -369,8 +371,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          acc[j + u][0] = mfma16x16x32(av[n & 1][u], pf[0][kk], acc[j + u][0]);
-          acc[j + u][1] = mfma16x16x32(av[n & 1][u], pf[1][kk], acc[j + u][1]);
+          acc[j + u][0] = E::mfma(av[n & 1][u], pf[0][kk], acc[j + u][0]);
+          acc[j + u][1] = E::mfma(av[n & 1][u], pf[1][kk], acc[j + u][1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -406,12 +408,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       for (int j = 0; j < S::JV; ++j) {
         const int dv = 16 * j + 4 * g4;
         if (dv < Dv) {
-          bf16x4 ov;
-          ov[0] = (__bf16)(acc[j][t][0] * inv);
-          ov[1] = (__bf16)(acc[j][t][1] * inv);
-          ov[2] = (__bf16)(acc[j][t][2] * inv);
-          ov[3] = (__bf16)(acc[j][t][3] * inv);
-          *reinterpret_cast<bf16x4*>(og + (int64_t)row * Dv + dv) = ov;
+          ushort4 ov;
+          ov.x = E::cvt(acc[j][t][0] * inv);
+          ov.y = E::cvt(acc[j][t][1] * inv);
+          ov.z = E::cvt(acc[j][t][2] * inv);
+          ov.w = E::cvt(acc[j][t][3] * inv);
+          *reinterpret_cast<ushort4*>(og + (int64_t)row * Dv + dv) = ov;
         }
       }
       if (g4 == 0) lg[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
@@ -425,8 +427,14 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)n_qt * p.Hq * p.B));
   Params arg = p;
   void* args[] = {&arg};
-  const void* fn = (p.D == DP && p.Dv == DVP) ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true>)
-                                              : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false>);
+  const bool exact = p.D == DP && p.Dv == DVP;
+  const void* fn;
+  if (p.f16)
+    fn = exact ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true>)
+               : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true>);
+  else
+    fn = exact ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false>)
+               : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false>);
   return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
 }
 

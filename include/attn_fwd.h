@@ -80,6 +80,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv, int Q,
                  int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream);
 
+/*
+ * Options of attn_fwd_ex (bit flags; 0 gives attn_fwd).
+ *   ATTN_FWD_FP16       q, k, v and o are IEEE binary16 instead of bfloat16,
+ *                       and the weights P are rounded to binary16 before
+ *                       the P.V product (the Laya "Fast backends" page,
+ *                       "Numerics", compares GPU results on inputs rounded to
+ *                       bf16 or fp16);
+ *   ATTN_FWD_FP32       q, k, v and o are float: the attn_fwd_f32 path;
+ *   ATTN_FWD_NONCAUSAL  no causal limit: every key k < K_b is legal for every
+ *                       row (LuisaCompute "Attention execution mapping"
+ *                       review, section 7, lists non-causal masks as the next
+ *                       semantics to add).  Rows have no legal key only when
+ *                       K_b == 0.  A window is measured back from the
+ *                       diagonal, so window > 0 with this flag is rejected.
+ * Everything else (layout, seqlens_k, ownership, scratch, status codes) is
+ * as for attn_fwd.  Unknown flag bits, FP16 together with FP32, or
+ * NONCAUSAL with window > 0 return ATTN_ERR_INVALID_ARG (nothing launched).
+ */
+enum attn_fwd_flags { ATTN_FWD_FP16 = 1, ATTN_FWD_FP32 = 2, ATTN_FWD_NONCAUSAL = 4 };
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
+                int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_fwd_strerror(int status);
 

@@ -75,6 +75,34 @@ def test_empty_problem_is_ok_without_launch(fn):
         assert fn(None, None, None, None, None, B, Hq, Hkv, Q, 8, 64, 64, None, 0, 1.0, None) == af.ATTN_OK
 
 
+def _ex(flags):
+    def fn(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seq, window, scale, stream):
+        return af.attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seq, window, scale, flags, stream)
+    return fn
+
+
+@pytest.mark.parametrize("flags", [af.ATTN_FWD_FP16, af.ATTN_FWD_NONCAUSAL, af.ATTN_FWD_FP32 | af.ATTN_FWD_NONCAUSAL])
+@pytest.mark.parametrize("case", BAD, ids=lambda c: "_".join(map(str, c[:8])))
+def test_ex_bad_arguments_rejected_before_launch(flags, case):
+    B, Hq, Hkv, Q, K, D, Dv, scale, want = case
+    fake = 1 << 20
+    assert _ex(flags)(fake, fake, fake, fake, fake, B, Hq, Hkv, Q, K, D, Dv, None, 0, scale, None) == want
+
+
+def test_ex_flag_checks():
+    fake = 1 << 20
+    args = (fake, fake, fake, fake, fake, 1, 4, 2, 8, 8, 64, 64, None)
+    bad = af.ATTN_ERR_INVALID_ARG
+    assert af.attn_fwd_ex(*args, 0, 1.0, 8, None) == bad                       # unknown bit
+    assert af.attn_fwd_ex(*args, 0, 1.0, -1, None) == bad
+    assert af.attn_fwd_ex(*args, 0, 1.0, af.ATTN_FWD_FP16 | af.ATTN_FWD_FP32, None) == bad
+    assert af.attn_fwd_ex(*args, 5, 1.0, af.ATTN_FWD_NONCAUSAL, None) == bad   # a window needs the causal limit
+    assert af.attn_fwd_ex(*args, 5, 1.0, af.ATTN_FWD_NONCAUSAL | af.ATTN_FWD_FP16, None) == bad
+    for flags in (0, af.ATTN_FWD_FP16, af.ATTN_FWD_FP32, af.ATTN_FWD_NONCAUSAL):
+        assert af.attn_fwd_ex(None, None, None, None, None, 2, 4, 2, 0, 8, 64, 64, None, 0, 1.0, flags,
+                              None) == af.ATTN_OK
+
+
 def test_slice_size_limit_boundary():
     # One row short of a 2 GiB (batch, head) slice is accepted by the plan.
     assert af.attn_fwd_plan(1, 4, 2, 8, (1 << 23) - 1, 128, 128)["path"] == af.PATH_PREFILL

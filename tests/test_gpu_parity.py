@@ -24,7 +24,7 @@ def _check(w, scale=None, window=None, orc=None, tag=""):
         f"seqlens={None if w.seqlens is None else list(w.seqlens)} scale={w.scale if scale is None else scale} {tag}")
     o, lse = run_gpu(w, q, k, v, scale=scale, window=window)
     ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window if window is None else window,
-                     scale=w.scale if scale is None else scale)
+                     scale=w.scale if scale is None else scale, causal=w.causal)
     return compare(o, lse, ro, rl, w.dtype, w.name + tag)
 
 
@@ -52,10 +52,41 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_shape_matrix(orc, shape, dtype):
     w = inputs.Workload("shape", *shape, dtype=dtype)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_noncausal_shape_matrix(orc, shape, dtype):
+    w = inputs.Workload("noncausal", *shape, dtype=dtype, causal=False)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("Q", [1, 3, 160])
+def test_noncausal_varlen(orc, Q, dtype):
+    sl = np.array([0, 1, 7, 64, 129, 160, 33, 0], np.int32)
+    w = inputs.Workload("noncausal_varlen", 8, 8, 2, Q, 160, 64, 64, dtype=dtype, seqlens=sl, causal=False)
+    _check(w, orc=orc)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Q", [1, 77])
+def test_fp16_scales(orc, scale, Q, causal):
+    w = inputs.Workload("f16_scale", 1, 4, 2, Q, 190, 64, 64, dtype="f16", causal=causal)
+    _check(w, scale=scale, orc=orc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("window", [1, 63, 1024])
+def test_fp16_window(orc, window, dtype):
+    sl = np.array([333, 0, 100], np.int32)
+    w = inputs.Workload("f16_window", 3, 4, 2, 200, 333, 64, 64, dtype=dtype, window=window, seqlens=sl)
     _check(w, orc=orc)
 
 
@@ -173,6 +204,21 @@ def test_forward_api_matches_raw_call(orc):
     ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens)
     compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl, "bf16",
             "forward()")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_forward_api_types_and_mask(orc, dtype, causal):
+    import torch
+    w = inputs.Workload("forward_ex", 2, 8, 2, 3, 150, 64, 64, dtype=dtype, causal=causal,
+                        seqlens=np.array([150, 90], np.int32))
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    o, lse = af.forward(to_dev(q), to_dev(k), to_dev(v), seqlens_k=to_dev(w.seqlens), causal=causal)
+    torch.cuda.synchronize()
+    assert o.dtype == {"f16": torch.float16, "f32": torch.float32}[dtype]
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, causal=causal)
+    compare(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl, dtype,
+            f"forward() {dtype} causal={causal}")
 
 
 def test_streams_are_honoured(orc):
