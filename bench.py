@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "causal GQA attn fwd: prefill TFLOP/s + decode KV GB/s, % of roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -74,12 +74,12 @@ class Problem:
         k = w.gen_k(padding="zero")
         v = w.gen_v(padding="zero")
         dev = "cuda:0"
-        self.q = torch.from_numpy(q).to(dev).view(torch.bfloat16)
-        self.k = torch.from_numpy(k).to(dev).view(torch.bfloat16)
-        self.v = torch.from_numpy(v).to(dev).view(torch.bfloat16)
+        as_dev = (lambda a: torch.from_numpy(a).to(dev).view(torch.bfloat16)) if w.dtype == "bf16" else \
+            (lambda a: torch.from_numpy(a).to(dev))
+        self.q, self.k, self.v = as_dev(q), as_dev(k), as_dev(v)
         self.host = (q, k, v)  # kept for the CPU baseline
         self.seq = None if w.seqlens is None else torch.from_numpy(np.asarray(w.seqlens, np.int32)).to(dev)
-        self.o = torch.empty(w.o_shape(), dtype=torch.bfloat16, device=dev)
+        self.o = torch.empty(w.o_shape(), dtype={"bf16": torch.bfloat16, "f16": torch.float16}[w.dtype], device=dev)
         self.lse = torch.empty((w.B, w.Hq, w.Q), dtype=torch.float32, device=dev)
         self.pairs = w.legal_pairs()
         self.flops = 2.0 * (w.D + w.Dv) * self.pairs
@@ -89,8 +89,13 @@ class Problem:
 
     def call(self, af, stream):
         w = self.w
-        st = af.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv,
-                         self.seq, w.window, w.scale, stream)
+        if w.dtype == "bf16" and w.causal:
+            st = af.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv,
+                             self.seq, w.window, w.scale, stream)
+        else:
+            flags = (af.ATTN_FWD_FP16 if w.dtype == "f16" else 0) | (0 if w.causal else af.ATTN_FWD_NONCAUSAL)
+            st = af.attn_fwd_ex(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv,
+                                self.seq, w.window, w.scale, flags, stream)
         if st != af.ATTN_OK:
             raise RuntimeError(f"attn_fwd failed on {w.name}: {af.strerror(st)}")
 
@@ -125,15 +130,56 @@ def cpu_baseline(probs, budget_s: float):
     return out, threads
 
 
+def run_options(args, torch, af, inputs):
+    """attn_fwd_ex options on the step's two shapes, each call timed alone: fp16
+    storage (causal prefill, decode) and the non-causal mode (bf16 prefill,
+    every key legal for every row)."""
+    import dataclasses
+    c3, c5 = inputs.config(3), inputs.config(5)
+    cases = [
+        ("prefill_f16", dataclasses.replace(c3, name="c3_shape_f16_causal_prefill", dtype="f16")),
+        ("prefill_noncausal", dataclasses.replace(c3, name="c3_shape_bf16_noncausal_prefill", causal=False)),
+        ("decode_f16", dataclasses.replace(c5, name="c5_shape_f16_decode", dtype="f16")),
+    ]
+    stream = torch.cuda.current_stream()
+    parts = {}
+    for tag, w in cases:
+        pr = Problem(w, torch)
+        for _ in range(args.warmup):
+            pr.call(af, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i].record(stream)
+            pr.call(af, stream)
+        ev[args.steps].record(stream)
+        torch.cuda.synchronize()
+        t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])) * 1e-3
+        if tag.startswith("prefill"):
+            achieved, peak, unit, bound = pr.flops / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = pr.kv_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+        parts[tag] = {"workload": w.name, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                      "frac": achieved / peak, "us_per_call": 1e6 * t}
+        log(f"[bench] {tag}: {1e6 * t:.1f} us/call, {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of peak")
+        del pr
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "attn_fwd_ex options: fp16 storage and non-causal mode, % of roofline",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "data": "synthetic: seeded N(0,1) rounded to the storage type (Philox-4x32-10, seed 1234)",
+                      "calls": parts, "kernel_digest": kernel_digest()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=500,
                     help="untimed steps first: the GPU clock settles under sustained load (about 0.5 s)")
-    ap.add_argument("--workload", choices=["step", "prefill", "decode", "copy"], default="step",
-                    help="time the whole step (default), one of its two calls alone (for profiling), or a "
-                         "plain 1 GiB device copy (to calibrate the HBM byte counters)")
+    ap.add_argument("--workload", choices=["step", "prefill", "decode", "copy", "options"], default="step",
+                    help="time the whole step (default), one of its two calls alone (for profiling), a "
+                         "plain 1 GiB device copy (to calibrate the HBM byte counters), or the attn_fwd_ex "
+                         "options (fp16 storage, non-causal) on the same two shapes, each call timed alone")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -162,6 +208,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": nbytes,
                           "bytes_written_per_dispatch": nbytes, "dispatches": args.warmup + args.steps}))
+        return
+    if args.workload == "options":
+        run_options(args, torch, af, inputs)
         return
     prefill_w, decode_w = inputs.config(3), inputs.config(5)
     probs = []
