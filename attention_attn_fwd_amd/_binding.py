@@ -21,7 +21,7 @@ PATH_NONE, PATH_PREFILL, PATH_DECODE = 0, 1, 2
 ATTN_FWD_FP16, ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL = 1, 2, 4
 
 # Every function the header declares; a CPU test checks the library exports all of them.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_strerror", "attn_fwd_plan")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_paged", "attn_fwd_strerror", "attn_fwd_plan")
 
 
 class AttnError(RuntimeError):
@@ -54,6 +54,8 @@ def load():
         lib.attn_fwd_f32.restype = ci
         lib.attn_fwd_ex.argtypes = sig[:-1] + [ci, vp]
         lib.attn_fwd_ex.restype = ci
+        lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, ci, ci, ci, vp, ci, cf, ci, vp]
+        lib.attn_fwd_paged.restype = ci
         lib.attn_fwd_strerror.argtypes = [ci]
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Plan)]
@@ -101,6 +103,14 @@ def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, sca
     """Raw C call with option flags (ATTN_FWD_FP16 / _FP32 / _NONCAUSAL); returns the status."""
     return load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
                               _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
+
+
+def attn_fwd_paged(q, k_pages, v_pages, o, lse, B, Hq, Hkv, Q, D, Dv, block_table, pages_per_seq, page_size,
+                   num_pages, seqlens_k, window, scale, flags, stream) -> int:
+    """Raw C call on a paged K/V cache; returns the status."""
+    return load().attn_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, D, Dv,
+                                 _ptr(block_table), int(pages_per_seq), int(page_size), int(num_pages),
+                                 _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
 
 
 def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
@@ -156,4 +166,45 @@ def forward(q, k, v, seqlens_k=None, window: int = 0, scale: Optional[float] = N
     st = attn_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags, stream)
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_ex")
+    return out, lse
+
+
+def forward_paged(q, k_pages, v_pages, block_table, seqlens_k=None, window: int = 0, scale: Optional[float] = None,
+                  out=None, lse=None, stream=None, causal: bool = True):
+    """Attention forward on a paged K/V cache (torch tensors on the GPU).
+
+    q [B,Hq,Q,D]; k_pages [num_pages,Hkv,page_size,D], v_pages
+    [num_pages,Hkv,page_size,Dv]; block_table int32 [B,pages_per_seq]: keys
+    j*page_size.. of sequence b are in page block_table[b,j].  bfloat16 or
+    float16.  Returns (o [B,Hq,Q,Dv], lse [B,Hq,Q] float32).
+    """
+    import torch
+
+    if q.dtype != k_pages.dtype or q.dtype != v_pages.dtype or q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q, k_pages, v_pages must all be bfloat16 or all float16")
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, Hq, Q, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_pages.shape
+    Dv = v_pages.shape[-1]
+    if tuple(v_pages.shape[:3]) != (num_pages, Hkv, page_size) or Dk != D:
+        raise ValueError(f"shape mismatch k_pages{tuple(k_pages.shape)} v_pages{tuple(v_pages.shape)}")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, pages_per_seq]")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or tuple(seqlens_k.shape) != (B,)):
+        raise ValueError("seqlens_k must be int32 [B] on the same device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, Q, Dv), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    flags = (ATTN_FWD_FP16 if q.dtype == torch.float16 else 0) | (0 if causal else ATTN_FWD_NONCAUSAL)
+    st = attn_fwd_paged(q, k_pages, v_pages, out, lse, B, Hq, Hkv, Q, D, Dv, block_table, block_table.shape[1],
+                        page_size, num_pages, seqlens_k, window, scale, flags, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_paged")
     return out, lse

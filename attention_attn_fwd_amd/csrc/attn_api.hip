@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -110,10 +111,17 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   return ATTN_OK;
 }
 
+// A paged K/V cache (null: contiguous k, v).
+struct PagedArgs {
+  const int32_t* block_table;
+  int pages_per_seq, page_shift, num_pages;
+};
+
 // flags: ATTN_FWD_FP16 / ATTN_FWD_FP32 select the element type (bf16 when
 // neither), ATTN_FWD_NONCAUSAL drops the causal limit.
 int run(int flags, const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
-        int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream_) {
+        int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream_,
+        const PagedArgs* paged = nullptr) {
   constexpr int kKnown = ATTN_FWD_FP16 | ATTN_FWD_FP32 | ATTN_FWD_NONCAUSAL;
   if ((flags & ~kKnown) != 0) return ATTN_ERR_INVALID_ARG;
   if ((flags & ATTN_FWD_FP16) && (flags & ATTN_FWD_FP32)) return ATTN_ERR_INVALID_ARG;
@@ -125,6 +133,7 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   if (st != ATTN_OK || plan.path == 0) return st;
   if (!q || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Hkv * K > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
+  if (paged && (int64_t)B * Hkv * K > 0 && !paged->block_table) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(o) || (k && !aligned16(k)) || (v && !aligned16(v)))
     return ATTN_ERR_INVALID_ARG;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -143,6 +152,12 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   p.scale_log2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
   p.scale = scale;
   p.rows = p.group * Q;
+  if (paged && K > 0) {
+    p.block_table = paged->block_table;
+    p.pages_per_seq = paged->pages_per_seq;
+    p.page_shift = paged->page_shift;
+    p.num_pages = paged->num_pages;
+  }
 
   if (!bf16) return launch_status(launch_fwd_f32(p, stream));
   if (plan.path == 1) return launch_status(launch_prefill_bf16(p, stream));
@@ -191,6 +206,23 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream) {
   return attn::run(flags, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+}
+
+int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse, int B, int Hq,
+                   int Hkv, int Q, int D, int Dv, const int32_t* block_table, int pages_per_seq, int page_size,
+                   int num_pages, const int32_t* seqlens_k, int window, float scale, int flags, void* stream) {
+  if (pages_per_seq < 0 || num_pages < 0 || page_size <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((page_size & (page_size - 1)) != 0 || page_size < (1 << attn::kMinPageShift) || page_size > (1 << 16))
+    return ATTN_ERR_UNSUPPORTED;
+  if (flags & ATTN_FWD_FP32) return ATTN_ERR_UNSUPPORTED;
+  const int64_t K = (int64_t)pages_per_seq * page_size;
+  if (K > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  if (K > 0 && num_pages == 0 && (int64_t)B * Hq * Q > 0) return ATTN_ERR_INVALID_ARG;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const attn::PagedArgs pg{block_table, pages_per_seq, shift, num_pages};
+  return attn::run(flags, q, k_pages, v_pages, o, lse, B, Hq, Hkv, Q, (int)K, D, Dv, seqlens_k, window, scale, stream,
+                   &pg);
 }
 
 const char* attn_fwd_strerror(int status) {

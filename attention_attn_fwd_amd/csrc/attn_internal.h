@@ -51,12 +51,24 @@ struct Params {
   float* ws_acc;           // [slots][rows][Dv] unnormalised P.V
   int n_workers;           // workgroups of the split pass (0: no keys at all)
   int rows;                // group * Q
+  // Paged K/V cache (block_table null: contiguous k [B,Hkv,K,D], v [B,Hkv,K,Dv]).
+  // Otherwise k [num_pages,Hkv,2^page_shift,D], v [num_pages,Hkv,2^page_shift,Dv]
+  // and keys [j << page_shift, (j + 1) << page_shift) of sequence b are in page
+  // block_table[b * pages_per_seq + j]; K = pages_per_seq << page_shift.
+  const int32_t* block_table;
+  int pages_per_seq;
+  int page_shift;
+  int num_pages;
 };
 
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const Params& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
+
+// Smallest page of a paged cache: a 64-key prefill block or an aligned 32-key
+// decode sub-block never straddles two pages.
+constexpr int kMinPageShift = 6;
 
 // Padded widths the kernels are instantiated for.
 inline int pad_width(int d) { return d <= 64 ? 64 : 128; }
@@ -83,6 +95,35 @@ __device__ __forceinline__ int clamp_len(const int32_t* seqlens, int b, int K) {
   if (!seqlens) return K;
   int s = seqlens[b];
   return s < 0 ? 0 : (s > K ? K : s);
+}
+
+// Page of a paged cache that holds key kb of sequence b (0 for a contiguous
+// cache).  A table entry outside [0, num_pages) is a caller error; it is
+// clamped so no load leaves the cache.
+__device__ __forceinline__ int kv_page(const Params& p, int b, int kb) {
+  if (!p.block_table) return 0;
+  const int pg = p.block_table[(int64_t)b * p.pages_per_seq + (kb >> p.page_shift)];
+  return pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+}
+
+// K and V rows of keys kb, kb + 1, ... of (sequence b, kv-head kh), with `page`
+// from kv_page(p, b, kb), and how many rows follow contiguously: to the end
+// of the slice, or of the page.
+struct KvSpan {
+  const uint16_t* k;
+  const uint16_t* v;
+  int rows;
+};
+__device__ __forceinline__ KvSpan kv_span(const Params& p, int b, int kh, int kb, int page) {
+  const uint16_t* k = static_cast<const uint16_t*>(p.k);
+  const uint16_t* v = static_cast<const uint16_t*>(p.v);
+  if (!p.block_table) {
+    const int64_t r = ((int64_t)b * p.Hkv + kh) * p.K + kb;
+    return KvSpan{k + r * p.D, v + r * p.Dv, p.K - kb};
+  }
+  const int off = kb & ((1 << p.page_shift) - 1);
+  const int64_t r = (((int64_t)page * p.Hkv + kh) << p.page_shift) + off;
+  return KvSpan{k + r * p.D, v + r * p.Dv, (1 << p.page_shift) - off};
 }
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]

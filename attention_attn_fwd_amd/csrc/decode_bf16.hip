@@ -52,12 +52,15 @@ struct DecodeShape {
   static_assert(Q_STAGE % 1024 == 0 && Q_LOADS <= K_LOADS, "Q tile uses the first K load offsets");
 };
 
-// Union of the legal key ranges of all rows of one (batch, kv-head) group:
-// [lo, hi).  Row q's position is q + K_b - Q, so the first row bounds the
-// window from below and the sequence end bounds everything from above.
+// Union of the legal key ranges of all rows of one (batch, kv-head) group,
+// widened down to a sub-block boundary: [lo, hi).  Row q's position is
+// q + K_b - Q, so the first row bounds the window from below and the sequence
+// end bounds everything from above.  Sub-blocks start at multiples of 32
+// keys, so none straddles a page of a paged cache; keys below the window
+// are masked like any other.
 __device__ __forceinline__ void group_key_range(int Kb, int Q, int W, int* lo, int* hi) {
   *hi = Kb;
-  *lo = W > 0 ? max(0, Kb - Q - W + 1) : 0;
+  *lo = (W > 0 ? max(0, Kb - Q - W + 1) : 0) & ~(kDecodeSub - 1);
 }
 
 // A sequence's groups: key range [lo, hi) with hi = K_b, and nsb sub-blocks.
@@ -210,14 +213,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   const uint32_t ring0 = lds_offset(ring);
   // Loads of the sub-block at cursor c into stage stg; with_q adds the Q rows
   // of c's group (rows past R read as zero).
-  auto issue = [&](const Cursor& c, int stg, bool with_q) {
+  // `page`: the page holding the sub-block's keys when the cache is paged.
+  auto issue = [&](const Cursor& c, int stg, bool with_q, int page) {
     const int kb0 = c.lo + c.sb * kDecodeSub;
-    const int64_t kv_slice = (int64_t)c.b * p.Hkv + c.kh;
-    const uint32_t rows_left = (uint32_t)(c.Kb - kb0);
-    const rsrc_t krs =
-        slice_rsrc(static_cast<const uint16_t*>(p.k) + (kv_slice * p.K + kb0) * p.D, rows_left * p.D * 2);
-    const rsrc_t vrs =
-        slice_rsrc(static_cast<const uint16_t*>(p.v) + (kv_slice * p.K + kb0) * p.Dv, rows_left * p.Dv * 2);
+    const KvSpan sp = kv_span(p, c.b, c.kh, kb0, page);
+    const uint32_t rows_left = (uint32_t)min(c.Kb - kb0, sp.rows);
+    const rsrc_t krs = slice_rsrc(sp.k, rows_left * p.D * 2);
+    const rsrc_t vrs = slice_rsrc(sp.v, rows_left * p.Dv * 2);
     const uint32_t st = ring0 + stg * S::STAGE;
 #pragma unroll
     for (int i = 0; i < S::K_LOADS; ++i) load_lds16(krs, st + i * 1024, koff[i]);
@@ -243,12 +245,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
   // carries Q (a group opens there), which fixes its number of loads.
   Cursor cc = start, ic = start;
   bool stage_q[2] = {false, false};
-  issue(ic, 0, true);
+  auto page_of = [&](const Cursor& c) {
+    return __builtin_amdgcn_readfirstlane(kv_page(p, c.b, c.lo + c.sb * kDecodeSub));
+  };
+  issue(ic, 0, true, page_of(ic));
   stage_q[0] = true;
   if (n > 1) {
     advance(ic);
     stage_q[1] = ic.sb == 0;
-    issue(ic, 1, stage_q[1]);
+    issue(ic, 1, stage_q[1], page_of(ic));
   }
 
   int stg = 0;
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       advance(ic);
       stage_q[stg] = ic.sb == 0;
-      issue(ic, stg, stage_q[stg]);
+      issue(ic, stg, stage_q[stg], page_of(ic));
     }
 
     // The piece of the group ends with its last sub-block or the share's.

@@ -116,10 +116,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int jb0 = kv_lo / BN;
   const int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
 
-  const int64_t kv_slice = (int64_t)b * p.Hkv + kh;
   const uint16_t* qg = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Q * D;
-  const uint16_t* kslice = static_cast<const uint16_t*>(p.k) + kv_slice * p.K * D;
-  const uint16_t* vslice = static_cast<const uint16_t*>(p.v) + kv_slice * p.K * Dv;
   uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Q * Dv;
   float* lg = p.lse + ((int64_t)b * p.Hq + h) * p.Q;
 
@@ -169,11 +166,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const uint32_t kstep = (uint32_t)(S::K_ROWS_PER_LOAD * D * 2);
   const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv * 2);
   const uint32_t lds0 = lds_offset(ring);
-  auto issue = [&](int jb, int stg) {
+  // Block jb's loads; `page` holds its keys when the cache is paged (blocks
+  // never straddle a page), read from the table a block ahead of its use.
+  auto issue = [&](int jb, int stg, int page) {
     const int kb0 = jb * BN;
-    const uint32_t rows_left = (uint32_t)(Kb - kb0);
-    const rsrc_t rk = slice_rsrc(kslice + (int64_t)kb0 * D, rows_left * D * 2);
-    const rsrc_t rv = slice_rsrc(vslice + (int64_t)kb0 * Dv, rows_left * Dv * 2);
+    const KvSpan sp = kv_span(p, b, kh, kb0, page);
+    const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
+    const rsrc_t rk = slice_rsrc(sp.k, rows_left * D * 2);
+    const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv * 2);
     const uint32_t base = lds0 + stg * S::STAGE + wave * 1024;
 #pragma unroll
     for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, base + i * 4096, koff + i * kstep);
@@ -378,8 +378,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       }
     }
   };
+  // pg_next: the page of block jb + 1 (a paged cache), read during block jb - 1.
+  int pg_next = 0;
   auto block = [&](int jb, auto stg_tag) {
-    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1);
+    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1, pg_next);
+    pg_next = jb + 2 < jb1 ? kv_page(p, b, (jb + 2) * BN) : 0;
     if (wave_sees(jb)) body(jb, stg_tag, wave_full(jb));
     // Block jb + 1 has landed for every wave, and every wave is done with
     // the stage of block jb, which the next block's loads overwrite.
@@ -388,7 +391,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   };
 
   if (jb0 < jb1) {
-    issue(jb0, 0);
+    issue(jb0, 0, kv_page(p, b, jb0 * BN));
+    pg_next = jb0 + 1 < jb1 ? kv_page(p, b, (jb0 + 1) * BN) : 0;
     wait_vmcnt<0>();
     __syncthreads();
   }

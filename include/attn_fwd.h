@@ -103,6 +103,27 @@ enum attn_fwd_flags { ATTN_FWD_FP16 = 1, ATTN_FWD_FP32 = 2, ATTN_FWD_NONCAUSAL =
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream);
 
+/*
+ * Paged K/V cache (block-table indirection, as a serving engine keeps it;
+ * the LuisaCompute review, section 7, names paged KV among the cases its
+ * validation matrix does not cover yet).  k_pages [num_pages, Hkv, page_size, D] and v_pages [num_pages, Hkv,
+ * page_size, Dv] (contiguous; a page holds page_size consecutive keys of
+ * every kv-head); block_table int32 [B, pages_per_seq] on the device: keys
+ * j*page_size .. (j+1)*page_size - 1 of sequence b are in page
+ * block_table[b*pages_per_seq + j].  The padded length is K = pages_per_seq *
+ * page_size; seqlens_k, window, scale, flags (ATTN_FWD_FP16,
+ * ATTN_FWD_NONCAUSAL) and everything else are as for attn_fwd_ex, computed
+ * exactly as attn_fwd_ex on the cache gathered into [B, Hkv, K, width].
+ * Pages may be shared between sequences.  page_size must be a power of two in
+ * [64, 65536] and the 16-bit types are required: otherwise
+ * ATTN_ERR_UNSUPPORTED.  A table entry outside [0, num_pages) is a caller
+ * error; the kernels clamp it so no load leaves the cache.  Table entries of
+ * pages past a sequence's K_b are never read.
+ */
+int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse, int B, int Hq,
+                   int Hkv, int Q, int D, int Dv, const int32_t* block_table, int pages_per_seq, int page_size,
+                   int num_pages, const int32_t* seqlens_k, int window, float scale, int flags, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_fwd_strerror(int status);
 

@@ -103,6 +103,27 @@ def test_ex_flag_checks():
                               None) == af.ATTN_OK
 
 
+def test_paged_argument_checks():
+    fake = 1 << 20
+
+    def paged(pps=4, page=64, npages=8, flags=0, window=0, table=fake, Q=8):
+        return af.attn_fwd_paged(fake, fake, fake, fake, fake, 1, 4, 2, Q, 64, 64, table, pps, page, npages, None,
+                                 window, 1.0, flags, None)
+    assert paged(page=96) == af.ATTN_ERR_UNSUPPORTED            # not a power of two
+    assert paged(page=32) == af.ATTN_ERR_UNSUPPORTED            # below 64
+    assert paged(page=1 << 17) == af.ATTN_ERR_UNSUPPORTED
+    assert paged(flags=af.ATTN_FWD_FP32) == af.ATTN_ERR_UNSUPPORTED
+    assert paged(page=0) == af.ATTN_ERR_INVALID_ARG
+    assert paged(pps=-1) == af.ATTN_ERR_INVALID_ARG
+    assert paged(npages=-1) == af.ATTN_ERR_INVALID_ARG
+    assert paged(npages=0) == af.ATTN_ERR_INVALID_ARG           # keys but no pages
+    assert paged(table=None) == af.ATTN_ERR_INVALID_ARG
+    assert paged(flags=af.ATTN_FWD_NONCAUSAL, window=3) == af.ATTN_ERR_INVALID_ARG
+    assert paged(flags=16) == af.ATTN_ERR_INVALID_ARG
+    assert paged(Q=0) == af.ATTN_OK                              # nothing to do
+    assert paged(pps=1 << 25, page=128) == af.ATTN_ERR_UNSUPPORTED  # K*D over the 2 GiB slice bound
+
+
 def test_slice_size_limit_boundary():
     # One row short of a 2 GiB (batch, head) slice is accepted by the plan.
     assert af.attn_fwd_plan(1, 4, 2, 8, (1 << 23) - 1, 128, 128)["path"] == af.PATH_PREFILL
