@@ -114,16 +114,23 @@ struct KvSpan {
   const uint16_t* v;
   int rows;
 };
-__device__ __forceinline__ KvSpan kv_span(const Params& p, int b, int kh, int kb, int page) {
+template <bool PAGED>
+__device__ __forceinline__ KvSpan kv_span_t(const Params& p, int b, int kh, int kb, int page) {
   const uint16_t* k = static_cast<const uint16_t*>(p.k);
   const uint16_t* v = static_cast<const uint16_t*>(p.v);
-  if (!p.block_table) {
+  if constexpr (!PAGED) {
+    (void)page;
     const int64_t r = ((int64_t)b * p.Hkv + kh) * p.K + kb;
     return KvSpan{k + r * p.D, v + r * p.Dv, p.K - kb};
+  } else {
+    (void)b;
+    const int off = kb & ((1 << p.page_shift) - 1);
+    const int64_t r = (((int64_t)page * p.Hkv + kh) << p.page_shift) + off;
+    return KvSpan{k + r * p.D, v + r * p.Dv, (1 << p.page_shift) - off};
   }
-  const int off = kb & ((1 << p.page_shift) - 1);
-  const int64_t r = (((int64_t)page * p.Hkv + kh) << p.page_shift) + off;
-  return KvSpan{k + r * p.D, v + r * p.Dv, (1 << p.page_shift) - off};
+}
+__device__ __forceinline__ KvSpan kv_span(const Params& p, int b, int kh, int kb, int page) {
+  return p.block_table ? kv_span_t<true>(p, b, kh, kb, page) : kv_span_t<false>(p, b, kh, kb, page);
 }
 
 // v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16]

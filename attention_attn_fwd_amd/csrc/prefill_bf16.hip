@@ -87,7 +87,8 @@ __device__ __forceinline__ void prefill_tile(const Params& p, int n_qt, int* qt,
 // EXACT: D == DP and Dv == DVP, so row strides are compile-time constants and
 // no channel is padding (the common case); otherwise padded channels read zero.
 // F16: the 16-bit inputs and output are IEEE binary16 instead of bf16.
-template <int DP, int DVP, bool EXACT, bool F16>
+// PAGED: K and V live in a paged cache (Params::block_table).
+template <int DP, int DVP, bool EXACT, bool F16, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   using S = PrefillShape<DP, DVP>;
   using E = Elem<F16>;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // never straddle a page), read from the table a block ahead of its use.
   auto issue = [&](int jb, int stg, int page) {
     const int kb0 = jb * BN;
-    const KvSpan sp = kv_span(p, b, kh, kb0, page);
+    const KvSpan sp = kv_span_t<PAGED>(p, b, kh, kb0, page);
     const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
     const rsrc_t rk = slice_rsrc(sp.k, rows_left * D * 2);
     const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv * 2);
@@ -378,11 +379,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       }
     }
   };
-  // pg_next: the page of block jb + 1 (a paged cache), read during block jb - 1.
-  int pg_next = 0;
+  // Paged cache: the page of block jb + 1 is loaded during block jb - 1 by a
+  // buffer load of this sequence's table row and settled after that block's
+  // closing wait, so no wait for it ever covers the next block's K/V loads.
+  // Without a table nothing is loaded (and the register the loads target is
+  // never written otherwise, so no wait is ever placed for it).
+  constexpr bool paged = PAGED;
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(p.block_table ? p.block_table + (int64_t)b * p.pages_per_seq : nullptr), (short)0,
+      p.block_table ? p.pages_per_seq * 4 : 0, kRsrcWord3);
+  auto page_fetch = [&](int jb) -> int {
+    return __builtin_amdgcn_raw_buffer_load_b32(trs, ((min(jb, jb1 - 1) * BN) >> p.page_shift) * 4, 0, 0);
+  };
+  auto page_settle = [&](int x) -> int {
+    launder(x);
+    const int pg = __builtin_amdgcn_readfirstlane(x);
+    return pg < 0 ? 0 : (pg >= p.num_pages ? max(p.num_pages - 1, 0) : pg);
+  };
+  int pg_next = 0;  // loaded, not yet settled
   auto block = [&](int jb, auto stg_tag) {
-    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1, pg_next);
-    pg_next = jb + 2 < jb1 ? kv_page(p, b, (jb + 2) * BN) : 0;
+    const int pg = paged ? page_settle(pg_next) : 0;
+    if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1, pg);
+    if (paged) pg_next = page_fetch(jb + 2);
     if (wave_sees(jb)) body(jb, stg_tag, wave_full(jb));
     // Block jb + 1 has landed for every wave, and every wave is done with
     // the stage of block jb, which the next block's loads overwrite.
@@ -391,8 +409,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   };
 
   if (jb0 < jb1) {
-    issue(jb0, 0, kv_page(p, b, jb0 * BN));
-    pg_next = jb0 + 1 < jb1 ? kv_page(p, b, (jb0 + 1) * BN) : 0;
+    if (paged) {
+      pg_next = page_fetch(jb0);
+      wait_vmcnt<0>();
+    }
+    issue(jb0, 0, paged ? page_settle(pg_next) : 0);
+    if (paged) pg_next = page_fetch(jb0 + 1);
     wait_vmcnt<0>();
     __syncthreads();
   }
@@ -431,14 +453,18 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)n_qt * p.Hq * p.B));
   Params arg = p;
   void* args[] = {&arg};
-  const bool exact = p.D == DP && p.Dv == DVP;
-  const void* fn;
-  if (p.f16)
-    fn = exact ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true>)
-               : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true>);
-  else
-    fn = exact ? reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false>)
-               : reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false>);
+  const void* const kernels[8] = {
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true, true>),
+  };
+  const int exact = p.D == DP && p.Dv == DVP;
+  const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
   return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
 }
 

@@ -87,9 +87,38 @@ class Problem:
         log(f"[bench] {w.name}: inputs ready in {time.time() - t0:.1f}s "
             f"(pairs {self.pairs}, flops {self.flops:.4e}, kv bytes {self.kv_bytes:.4e})")
 
+    def paginate(self, page, torch):
+        """Move K/V into a paged cache: every page of a sequence's first K_b keys,
+        in a seeded random order; the calls then go through attn_fwd_paged."""
+        w = self.w
+        q, k, v = self.host
+        rng = np.random.default_rng(1234)
+        pps = w.K // page
+        used = [(b, j) for b in range(w.B) for j in range(pps) if j * page < w.kb(b)]
+        order = rng.permutation(len(used))
+        kp = np.zeros((len(used), w.Hkv, page, w.D), dtype=k.dtype)
+        vp = np.zeros((len(used), w.Hkv, page, w.Dv), dtype=v.dtype)
+        table = np.zeros((w.B, pps), dtype=np.int32)
+        for i, (b, j) in enumerate(used):
+            pg = int(order[i])
+            table[b, j] = pg
+            kp[pg] = k[b, :, j * page:(j + 1) * page]
+            vp[pg] = v[b, :, j * page:(j + 1) * page]
+        as_dev = (lambda a: torch.from_numpy(a).to("cuda:0").view(torch.bfloat16)) if w.dtype == "bf16" else \
+            (lambda a: torch.from_numpy(a).to("cuda:0"))
+        self.k, self.v = as_dev(kp), as_dev(vp)
+        self.table = torch.from_numpy(table).to("cuda:0")
+        self.page, self.num_pages = page, len(used)
+        self.host = None
+
     def call(self, af, stream):
         w = self.w
-        if w.dtype == "bf16" and w.causal:
+        if getattr(self, "page", None):
+            flags = (af.ATTN_FWD_FP16 if w.dtype == "f16" else 0) | (0 if w.causal else af.ATTN_FWD_NONCAUSAL)
+            st = af.attn_fwd_paged(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.D, w.Dv,
+                                   self.table, w.K // self.page, self.page, self.num_pages, self.seq, w.window,
+                                   w.scale, flags, stream)
+        elif w.dtype == "bf16" and w.causal:
             st = af.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv,
                              self.seq, w.window, w.scale, stream)
         else:
@@ -131,9 +160,10 @@ def cpu_baseline(probs, budget_s: float):
 
 
 def run_options(args, torch, af, inputs):
-    """attn_fwd_ex options on the step's two shapes, each call timed alone: fp16
-    storage (causal prefill, decode) and the non-causal mode (bf16 prefill,
-    every key legal for every row)."""
+    """attn_fwd_ex / attn_fwd_paged options on the step's two shapes, each call
+    timed alone: fp16 storage (causal prefill, decode), the non-causal mode
+    (bf16 prefill, every key legal for every row), and a paged K/V cache
+    (pages of 256 keys for the prefill, 128 for the decode, in random order)."""
     import dataclasses
     c3, c5 = inputs.config(3), inputs.config(5)
     cases = [
@@ -141,10 +171,15 @@ def run_options(args, torch, af, inputs):
         ("prefill_noncausal", dataclasses.replace(c3, name="c3_shape_bf16_noncausal_prefill", causal=False)),
         ("decode_f16", dataclasses.replace(c5, name="c5_shape_f16_decode", dtype="f16")),
     ]
+    cases += [("prefill_paged", dataclasses.replace(c3, name="c3_paged256_prefill")),
+              ("decode_paged", dataclasses.replace(c5, name="c5_paged128_decode"))]
+    pages = {"prefill_paged": 256, "decode_paged": 128}
     stream = torch.cuda.current_stream()
     parts = {}
     for tag, w in cases:
         pr = Problem(w, torch)
+        if tag in pages:
+            pr.paginate(pages[tag], torch)
         for _ in range(args.warmup):
             pr.call(af, stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -164,7 +199,7 @@ def run_options(args, torch, af, inputs):
         log(f"[bench] {tag}: {1e6 * t:.1f} us/call, {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of peak")
         del pr
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "attn_fwd_ex options: fp16 storage and non-causal mode, % of roofline",
+    print(json.dumps({"metric": "options: fp16 storage, non-causal mode, paged K/V cache, % of roofline",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic: seeded N(0,1) rounded to the storage type (Philox-4x32-10, seed 1234)",
                       "calls": parts, "kernel_digest": kernel_digest()}), flush=True)
