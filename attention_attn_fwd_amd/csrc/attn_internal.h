@@ -22,7 +22,10 @@ constexpr int kPrefillBN = 64;                                   // keys per blo
 // equal share of all (batch, kv-head) groups' sub-blocks.
 constexpr int kDecodeSub = 32;
 constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
-constexpr int kDecodeMaxQ = 4;
+// Any Q whose g*Q rows fit the two 16-row MFMA tiles takes the split-KV path
+// (decode Q = 1..4, and the short query runs of speculative decoding or
+// chunked prefill): the packed rows share each K/V read.
+constexpr int kDecodeMaxQ = kDecodeMaxRows;
 // Each worker of the split pass takes at least kDecodeMinShare sub-blocks.
 constexpr int kDecodeMinShare = 4;
 

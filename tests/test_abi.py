@@ -126,7 +126,8 @@ def test_paged_argument_checks():
 
 def test_slice_size_limit_boundary():
     # One row short of a 2 GiB (batch, head) slice is accepted by the plan.
-    assert af.attn_fwd_plan(1, 4, 2, 8, (1 << 23) - 1, 128, 128)["path"] == af.PATH_PREFILL
+    assert af.attn_fwd_plan(1, 4, 2, 64, (1 << 23) - 1, 128, 128)["path"] == af.PATH_PREFILL
+    assert af.attn_fwd_plan(1, 4, 2, 8, (1 << 23) - 1, 128, 128)["path"] == af.PATH_DECODE
     with pytest.raises(af.AttnError) as e:
         af.attn_fwd_plan(1, 4, 2, 8, 1 << 23, 128, 128)
     assert e.value.status == af.ATTN_ERR_UNSUPPORTED
@@ -144,7 +145,9 @@ def test_plan_selects_paths():
     assert af.attn_fwd_plan(1, 8, 2, 1, 2053, 80, 96)["path"] == af.PATH_DECODE
     assert af.attn_fwd_plan(1, 8, 2, 4, 100, 64, 64)["path"] == af.PATH_DECODE      # 16 packed rows
     assert af.attn_fwd_plan(1, 64, 1, 1, 100, 64, 64)["path"] == af.PATH_PREFILL    # 64 rows: prefill kernel
-    assert af.attn_fwd_plan(1, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_PREFILL
+    assert af.attn_fwd_plan(1, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_DECODE      # 20 packed rows
+    assert af.attn_fwd_plan(1, 2, 2, 32, 100, 64, 64)["path"] == af.PATH_DECODE     # Q = 32, MHA
+    assert af.attn_fwd_plan(1, 8, 2, 9, 100, 64, 64)["path"] == af.PATH_PREFILL     # 36 rows
     assert af.attn_fwd_plan(0, 8, 2, 5, 100, 64, 64)["path"] == af.PATH_NONE
     assert af.attn_fwd_plan(1, 8, 2, 1, 0, 64, 64)["split_workers"] == 0
     with pytest.raises(af.AttnError):

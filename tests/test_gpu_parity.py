@@ -59,6 +59,22 @@ def test_shape_matrix(orc, shape, dtype):
     _check(w, orc=orc)
 
 
+# Short query runs (speculative decoding, chunked prefill) on the split-KV
+# path: any Q with g*Q <= 32, causal and not, varlen with empty sequences.
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 5, 2053, 128, 128), (3, 4, 1, 8, 700, 64, 64),
+                                   (2, 2, 2, 32, 300, 128, 128), (2, 16, 4, 7, 1500, 80, 96),
+                                   (1, 32, 8, 8, 33, 64, 64)], ids=lambda s: "x".join(map(str, s)))
+def test_short_query_runs(orc, shape, causal):
+    B = shape[0]
+    sl = np.linspace(0, shape[4], B).astype(np.int32) if B > 2 else np.array([shape[4], 3], np.int32)[:B]
+    w = inputs.Workload("short_q", *shape, seqlens=sl, causal=causal)
+    assert af.attn_fwd_plan(*shape)["path"] == af.PATH_DECODE
+    _check(w, orc=orc)
+    if causal:
+        _check(w, window=17, orc=orc, tag=" W=17")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_noncausal_shape_matrix(orc, shape, dtype):
