@@ -79,6 +79,33 @@ int split_workers(int B, int Hkv, int K, int D, int Dv, int rows) {
   return (int)std::max<int64_t>(1, std::min(w, resident));
 }
 
+// Key-range pieces per prefill tile.  The kernel holds two workgroups per CU
+// (512 on the chip); while the tiles alone fill fewer than that, each tile's
+// range is cut so that tiles x pieces reaches about 512, keeping at least
+// kPrefillMinSplitBlocks 64-key blocks per piece so the partial states (the
+// fp32 accumulator of 128 rows, written and read back once: about an eighth
+// of the K/V bytes such a piece streams at D = Dv = 128) and the combine
+// launch stay small next to the piece.  If that leaves some of the 256 CUs
+// without a workgroup, pieces down to kPrefillMinSplitBlocksIdle blocks are
+// taken to reach 256.  (Measured on MI355X: with 256 workgroups already
+// running, 16-block pieces lost to 32-block ones; with 16 running, 16-block
+// pieces won; 8-block pieces never paid for the combine launch.)
+// ATTN_FWD_PREFILL_SPLITS (>= 1) overrides it.
+int prefill_splits(int B, int Hkv, int Q, int group, int K) {
+  if (K <= 0) return 1;
+  if (const char* e = std::getenv("ATTN_FWD_PREFILL_SPLITS")) {
+    const int v = std::atoi(e);
+    if (v >= 1) return std::min(v, kPrefillMaxSplits);
+  }
+  const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
+  constexpr int64_t kSlots = 512, kCUs = 256;
+  if (tiles >= kSlots) return 1;
+  const int64_t blocks = ((int64_t)K + kPrefillBN - 1) / kPrefillBN;
+  int64_t s = std::min((kSlots + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocks);
+  if (tiles * s < kCUs) s = std::max(s, std::min((kCUs + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocksIdle));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, kPrefillMaxSplits));
+}
+
 // Checks shared by both entry points; fills the plan.
 int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, float scale, bool bf16,
                    attn_fwd_plan_t* plan) {
@@ -106,7 +133,18 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   } else {
     plan->path = 1;
     const int bm = bf16 ? kPrefillBM : kF32Rows;
-    if ((int64_t)((Q + bm - 1) / bm) * Hq * B > (int64_t)UINT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    // Workgroup indices are int; a split pass launches fewer than 512 tiles
+    // times at most kPrefillMaxSplits pieces.
+    if ((int64_t)((Q + bm - 1) / bm) * Hq * B > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    if (bf16) {
+      const int ns = prefill_splits(B, Hkv, Q, group, K);
+      plan->split_workers = ns;
+      if (ns > 1) {
+        const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
+        plan->partial_slots = (int)(tiles * ns);
+        plan->workspace_bytes = (int64_t)plan->partial_slots * kPrefillBM * (Dv + 2) * 4;
+      }
+    }
   }
   return ATTN_OK;
 }
@@ -159,12 +197,19 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
     p.num_pages = paged->num_pages;
   }
 
+  p.n_split = 1;
   if (!bf16) return launch_status(launch_fwd_f32(p, stream));
-  if (plan.path == 1) return launch_status(launch_prefill_bf16(p, stream));
+  if (plan.path == 1 && plan.split_workers <= 1) return launch_status(launch_prefill_bf16(p, stream));
 
-  // Split-KV decode: scratch from the device's stream-ordered pool.
-  p.n_workers = plan.split_workers;
-  const int64_t parts = (int64_t)plan.partial_slots * p.rows;
+  // Split-KV decode or prefill: scratch from the device's stream-ordered pool.
+  int64_t parts;
+  if (plan.path == 1) {
+    p.n_split = plan.split_workers;
+    parts = (int64_t)plan.partial_slots * kPrefillBM;
+  } else {
+    p.n_workers = plan.split_workers;
+    parts = (int64_t)plan.partial_slots * p.rows;
+  }
   const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
   if (fail && fail[0] == '1') return ATTN_ERR_OOM;
   void* ws = nullptr;
@@ -180,7 +225,7 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   p.ws_acc = wsf;  // [parts][Dv] first: 16-byte aligned rows
   p.ws_m = wsf + parts * Dv;
   p.ws_l = p.ws_m + parts;
-  const int launched = launch_status(launch_decode_bf16(p, stream));
+  const int launched = launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
   if (ws) {
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;

@@ -18,6 +18,30 @@ constexpr int kPrefillRowsPerWave = 32;
 constexpr int kPrefillBM = kPrefillWaves * kPrefillRowsPerWave;  // query rows per workgroup
 constexpr int kPrefillBN = 64;                                   // keys per block
 
+// Prefill tiles: each covers 128 rows of the row list of one (batch, kv-head)
+// group.  Row r of the list is query row r % Q of query head h_base + r / Q.
+// Per-head tiles (the list is one head's Q rows) are used when Q >= 128 or
+// the group has one head; packed tiles (the list is the g*Q rows of the
+// group's heads, head-major) when a head has fewer rows than a tile, so one
+// tile holds the rows of several heads, which share every K/V block (the
+// short query runs of chunked prefill and speculative decoding).
+__host__ __device__ inline bool prefill_packed(int Q, int group) { return group > 1 && Q < kPrefillBM; }
+// Tiles of one (batch, kv-head) group.
+__host__ __device__ inline int prefill_group_tiles(int Q, int group) {
+  const int n_qt = (Q + kPrefillBM - 1) / kPrefillBM;
+  return prefill_packed(Q, group) ? (group * Q + kPrefillBM - 1) / kPrefillBM : group * n_qt;
+}
+// Split-KV prefill: when the tiles alone leave most workgroup slots of the
+// chip idle (few long sequences), each tile's key range is cut into n_split
+// contiguous pieces of whole blocks, processed by separate workgroups that
+// write fp32 partial states; a combine pass merges them.  At most
+// kPrefillMaxSplits pieces, each at least kPrefillMinSplitBlocks blocks
+// (kPrefillMinSplitBlocksIdle while the pieces would not give every CU a
+// workgroup).
+constexpr int kPrefillMaxSplits = 32;
+constexpr int kPrefillMinSplitBlocks = 32;
+constexpr int kPrefillMinSplitBlocksIdle = 16;
+
 // Split-KV decode: single-wave workers streaming 32-key sub-blocks, each an
 // equal share of all (batch, kv-head) groups' sub-blocks.
 constexpr int kDecodeSub = 32;
@@ -48,12 +72,15 @@ struct Params {
   int q_sign;              // 0x8000 when the scale is negative (q is negated), else 0
   float scale_log2;        // |scale| * log2(e)
   float scale;             // raw scale (fp32 path)
-  // split-KV decode scratch: one partial per (slot, row), slot = group + worker
+  // Split-KV scratch.  Decode: one partial per (slot, row), slot = group +
+  // worker.  Prefill: one per (part, tile row), part = (group * n_split +
+  // split) * tiles per group + tile, tile row in [0, 128).
   float* ws_m;             // [slots][rows]  running max, log2 units
   float* ws_l;             // [slots][rows]  sum of 2^(s*c - m)
   float* ws_acc;           // [slots][rows][Dv] unnormalised P.V
   int n_workers;           // workgroups of the split pass (0: no keys at all)
   int rows;                // group * Q
+  int n_split;             // prefill: key-range pieces per tile (1: no split)
   // Paged K/V cache (block_table null: contiguous k [B,Hkv,K,D], v [B,Hkv,K,Dv]).
   // Otherwise k [num_pages,Hkv,2^page_shift,D], v [num_pages,Hkv,2^page_shift,Dv]
   // and keys [j << page_shift, (j + 1) << page_shift) of sequence b are in page

@@ -5,10 +5,17 @@
 // load K/V -> QK -> mask -> max/exp/sum -> rescale -> PV -> update).
 //
 // Mapping on CDNA4:
-//   * one workgroup = 4 waves = 128 query rows of one (batch, head); each wave
-//     owns 32 rows as two 16-column MFMA tiles, Q held in registers; two
-//     workgroups share a CU, so each SIMD runs one wave of each and the
-//     softmax of one overlaps the matrix products of the other;
+//   * one workgroup = 4 waves = a tile of 128 query rows of one (batch,
+//     kv-head) group: rows of one query head, or, when a head has fewer than
+//     128 rows, the rows of several heads of the group (they read the same
+//     K/V, section 5 of the review); each wave owns 32 rows as two 16-column
+//     MFMA tiles, Q held in registers; two workgroups share a CU, so each
+//     SIMD runs one wave of each and the softmax of one overlaps the matrix
+//     products of the other;
+//   * when the tiles are too few to fill the GPU (few long sequences), each
+//     tile's key range is cut into pieces run by separate workgroups, which
+//     write their (row_max, row_sum, acc) state in fp32; a combine pass merges
+//     the pieces of a row in order (the legal merge of section 5);
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16, so each lane holds 16 keys of
 //     one query column and the row max/sum is in-lane plus two permlane swaps;
 //     P^T stays in that register layout and feeds O^T = V^T P^T directly, V^T
@@ -58,29 +65,73 @@ struct PrefillShape {
   static_assert(LDS <= 65536, "ds_read immediate offsets cover the ring");
 };
 
-// Block index -> (query tile, batch, head).  When the (batch, kv-head) groups
-// divide evenly over the 8 XCDs (workgroup i runs on XCD i % 8), each XCD gets
-// whole groups and finishes one group (all its query heads and tiles,
-// heaviest tile first) before the next, so the workgroups resident on an XCD
-// stream the same K/V slice through its L2; otherwise the order is heaviest
-// tile first with heads fastest.
-__device__ __forceinline__ void prefill_tile(const Params& p, int n_qt, int* qt, int* b, int* h) {
-  const int x = blockIdx.x;
-  const int groups = p.B * p.Hkv;
-  if ((groups & 7) == 0) {
-    const int xcd = x & 7, slot = x >> 3;
-    const int per_grp = p.group * n_qt;
-    const int gi = slot / per_grp, rem = slot - gi * per_grp;
-    const int qrank = rem / p.group;
-    const int grp = gi * 8 + xcd;
-    *b = grp / p.Hkv;
-    *h = (grp - *b * p.Hkv) * p.group + rem % p.group;
-    *qt = n_qt - 1 - qrank;
+// A tile: rows [r0, r0 + 128) of the row list of one (batch, kv-head) group
+// (n_rows rows, row r = query row r % Q of head h_base + r / Q), and the
+// piece `split` of its key range.  `part` numbers (group, split, tile)
+// triples; it indexes the partial states of a split pass.
+struct PrefillTile {
+  int b, kh, h_base, r0, n_rows, split, part;
+};
+
+// Tile `rem` of group `grp` (rank order: heaviest causal tile first, heads
+// fastest among per-head tiles).
+__device__ __forceinline__ PrefillTile prefill_tile_of(const Params& p, int grp, int rem) {
+  PrefillTile t;
+  t.b = grp / p.Hkv;
+  t.kh = grp - t.b * p.Hkv;
+  if (prefill_packed(p.Q, p.group)) {
+    t.h_base = t.kh * p.group;
+    t.n_rows = p.group * p.Q;
+    t.r0 = (prefill_group_tiles(p.Q, p.group) - 1 - rem) * kPrefillBM;
   } else {
-    *h = x % p.Hq;
-    const int y = x / p.Hq;
-    *b = y % p.B;
-    *qt = n_qt - 1 - y / p.B;
+    const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
+    const int qrank = rem / p.group;
+    t.h_base = t.kh * p.group + (rem - qrank * p.group);
+    t.n_rows = p.Q;
+    t.r0 = (n_qt - 1 - qrank) * kPrefillBM;
+  }
+  t.split = 0;
+  t.part = 0;
+  return t;
+}
+
+// Block index -> tile.  A virtual group is a (group, split) pair.  When the
+// virtual groups divide evenly over the 8 XCDs (workgroup i runs on XCD
+// i % 8), each XCD gets whole virtual groups and finishes one (all its
+// tiles, heaviest first) before the next, so the workgroups resident on an
+// XCD stream the same K/V through its L2; otherwise the order is heaviest
+// tile first with virtual groups fastest.
+__device__ __forceinline__ PrefillTile prefill_tile(const Params& p) {
+  const int x = blockIdx.x;
+  const int vgroups = p.B * p.Hkv * p.n_split;
+  const int per_grp = prefill_group_tiles(p.Q, p.group);
+  int vg, rem;
+  if ((vgroups & 7) == 0) {
+    const int xcd = x & 7, slot = x >> 3;
+    const int gi = slot / per_grp;
+    rem = slot - gi * per_grp;
+    vg = gi * 8 + xcd;
+  } else {
+    rem = x / vgroups;
+    vg = x - rem * vgroups;
+  }
+  const int grp = vg / p.n_split;
+  PrefillTile t = prefill_tile_of(p, grp, rem);
+  t.split = vg - grp * p.n_split;
+  t.part = vg * per_grp + rem;
+  return t;
+}
+
+// Query rows r0 .. r1 of a row list (r0 <= r1) lie at positions q + delta with
+// q in [qlo, qhi]: the exact range when the rows belong to one head, else the
+// whole head.
+__device__ __forceinline__ void row_q_range(int r0, int r1, int Q, int* qlo, int* qhi) {
+  if (r0 / Q == r1 / Q) {
+    *qlo = r0 % Q;
+    *qhi = r1 % Q;
+  } else {
+    *qlo = 0;
+    *qhi = Q - 1;
   }
 }
 
@@ -101,44 +152,61 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
-  int qt, b, h;
-  prefill_tile(p, n_qt, &qt, &b, &h);
-  const int kh = h / p.group;
+  const PrefillTile tile = prefill_tile(p);
+  const int b = tile.b, kh = tile.kh, Q = p.Q;
 
   const int Kb = clamp_len(p.seqlens, b, p.K);
-  const int delta = row_delta(Kb, p.Q, p.causal_shift);  // absolute position of row q is q + delta
+  const int delta = row_delta(Kb, Q, p.causal_shift);  // absolute position of query row q is q + delta
   const int W = p.window;
-  const int q0 = qt * kPrefillBM;
-  const int q_end = min(q0 + kPrefillBM, p.Q);
 
-  const int kv_hi = min(Kb, q_end - 1 + delta + 1);
-  const int kv_lo = W > 0 ? max(0, q0 + delta - W + 1) : 0;
-  const int jb0 = kv_lo / BN;
-  const int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
+  // The tile's rows and their query positions bound its KV range.
+  const int t_last = min(tile.r0 + kPrefillBM, tile.n_rows) - 1;
+  int tq_lo, tq_hi;
+  row_q_range(tile.r0, t_last, Q, &tq_lo, &tq_hi);
+  const int kv_hi = min(Kb, tq_hi + delta + 1);
+  const int kv_lo = W > 0 ? max(0, tq_lo + delta - W + 1) : 0;
+  int jb0 = kv_lo / BN;
+  int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
+  if (p.n_split > 1) {  // this workgroup's piece: blocks split as evenly as they go
+    const int nb = jb1 - jb0, s0 = jb0;
+    jb0 = s0 + (int)((int64_t)nb * tile.split / p.n_split);
+    jb1 = s0 + (int)((int64_t)nb * (tile.split + 1) / p.n_split);
+  }
 
-  const uint16_t* qg = static_cast<const uint16_t*>(p.q) + ((int64_t)b * p.Hq + h) * p.Q * D;
-  uint16_t* og = static_cast<uint16_t*>(p.o) + ((int64_t)b * p.Hq + h) * p.Q * Dv;
-  float* lg = p.lse + ((int64_t)b * p.Hq + h) * p.Q;
-
-  // Wave-level (scalar) row range and absolute positions.
-  const int qw0 = q0 + wave * kPrefillRowsPerWave;
-  const bool wave_has_rows = qw0 < p.Q;
-  const int qw_last = min(qw0 + kPrefillRowsPerWave, p.Q) - 1;
-  const int pw_first = qw0 + delta, pw_last = qw_last + delta;
+  // Wave-level (scalar) row range and the positions its rows span.
+  const int rw0 = tile.r0 + wave * kPrefillRowsPerWave;
+  const bool wave_has_rows = rw0 < tile.n_rows;
+  int qw_lo = 0, qw_hi = 0;
+  if (wave_has_rows) row_q_range(rw0, min(rw0 + kPrefillRowsPerWave, tile.n_rows) - 1, Q, &qw_lo, &qw_hi);
+  const int pw_first = qw_lo + delta, pw_last = qw_hi + delta;
   const float c = p.scale_log2;
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
+
+  // This lane's two rows (one per 16-row MFMA tile): query row q_row[t] of
+  // head h_base + hh_row[t]; row_ok[t] false past the row list.
+  int q_row[2], hh_row[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = rw0 + 16 * t + l16;
+    row_ok[t] = r < tile.n_rows;
+    hh_row[t] = r / Q;
+    q_row[t] = r - hh_row[t] * Q;
+  }
+  auto row_index = [&](int t) {  // flat (b, head, q) row of O and LSE
+    return ((int64_t)b * p.Hq + tile.h_base + hh_row[t]) * Q + q_row[t];
+  };
 
   // Q fragments (B operand of S^T = K Q^T): lane holds row l16 of the tile,
   // channels 32s + 8*g4 .. +7.
   bf16x8 qf[2][S::KS];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = qw0 + 16 * t + l16;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + row_index(t) * D;
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
       const int col = 32 * s + 8 * g4;
-      uint4 u = (row < p.Q && col < D) ? load_u4(qg + (int64_t)row * D + col) : zero_u4();
+      uint4 u = (row_ok[t] && col < D) ? load_u4(qrow + col) : zero_u4();
       u.x ^= qx; u.y ^= qx; u.z ^= qx; u.w ^= qx;
       qf[t][s] = __builtin_bit_cast(bf16x8, u);
     }
@@ -225,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   auto mask_bias = [&](int kb0, f32x4 (&s)[4][2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int rel = qw0 + 16 * t + l16 + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
+      const int rel = q_row[t] + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
       const int hi = min(rel, Kb - kb0 - 4 * g4 - 1);
       const int lo = W > 0 ? max(rel - W + 1, 0) : 0;
       const uint32_t span = (uint32_t)(hi - lo);
@@ -424,12 +492,37 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   }
 
   if (!wave_has_rows) return;
+  if (p.n_split > 1) {
+    // Partial state of this piece: (m, l) and the unnormalised acc; a row
+    // that saw no legal key gets m = -inf, l = 0 and no acc.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float lt = group4_sum(l_run[t]);
+      if (row_ok[t]) {
+        const int64_t slot = (int64_t)tile.part * kPrefillBM + (rw0 - tile.r0) + 16 * t + l16;
+        if (g4 == 0) {
+          p.ws_m[slot] = lt > 0.f ? m_run[t] : -INFINITY;
+          p.ws_l[slot] = lt;
+        }
+        if (lt > 0.f) {
+          float* arow = p.ws_acc + slot * Dv;
+#pragma unroll
+          for (int j = 0; j < S::JV; ++j) {
+            const int dv = 16 * j + 4 * g4;
+            if (dv < Dv) *reinterpret_cast<f32x4*>(arow + dv) = acc[j][t];
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float lt = group4_sum(l_run[t]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int row = qw0 + 16 * t + l16;
-    if (row < p.Q) {
+    if (row_ok[t]) {
+      const int64_t row = row_index(t);
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + row * Dv;
 #pragma unroll
       for (int j = 0; j < S::JV; ++j) {
         const int dv = 16 * j + 4 * g4;
@@ -439,18 +532,67 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
           ov.y = E::cvt(acc[j][t][1] * inv);
           ov.z = E::cvt(acc[j][t][2] * inv);
           ov.w = E::cvt(acc[j][t][3] * inv);
-          *reinterpret_cast<ushort4*>(og + (int64_t)row * Dv + dv) = ov;
+          *reinterpret_cast<ushort4*>(orow + dv) = ov;
         }
       }
-      if (g4 == 0) lg[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+      if (g4 == 0) p.lse[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 }
 
+// Combine pass of split-KV prefill: one wave per tile row merges the row's
+// n_split partial states in split order (the merge of two online-softmax
+// states: rescale both to the larger max, add sums and accumulators), then
+// normalises and writes O and the LSE.  Lane l owns channels 2l, 2l + 1.
+template <bool F16>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
+  using E = Elem<F16>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int per_grp = prefill_group_tiles(p.Q, p.group);
+  const int r_local = (int)(wid % kPrefillBM);
+  const int64_t tg = wid / kPrefillBM;
+  const int rem = (int)(tg % per_grp), grp = (int)(tg / per_grp);
+  if (grp >= p.B * p.Hkv) return;
+  const PrefillTile tile = prefill_tile_of(p, grp, rem);
+  const int r = tile.r0 + r_local;
+  if (r >= tile.n_rows) return;
+  const int hh = r / p.Q, q = r - hh * p.Q;
+  const int64_t row = ((int64_t)tile.b * p.Hq + tile.h_base + hh) * p.Q + q;
+  auto slot_of = [&](int s) { return ((int64_t)(grp * p.n_split + s) * per_grp + rem) * kPrefillBM + r_local; };
+
+  float mx = -INFINITY;
+  for (int s = 0; s < p.n_split; ++s) mx = fmaxf(mx, p.ws_m[slot_of(s)]);
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  const int dv = 2 * lane;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < p.n_split; ++s) {
+      const int64_t slot = slot_of(s);
+      const float ms = p.ws_m[slot];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - mx);
+      l += p.ws_l[slot] * w;
+      if (dv < p.Dv) {
+        const float2 a = *reinterpret_cast<const float2*>(p.ws_acc + slot * p.Dv + dv);
+        o0 += a.x * w;
+        o1 += a.y * w;
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (dv < p.Dv) {
+    ushort2 ov;
+    ov.x = E::cvt(o0 * inv);
+    ov.y = E::cvt(o1 * inv);
+    *reinterpret_cast<ushort2*>(static_cast<uint16_t*>(p.o) + row * p.Dv + dv) = ov;
+  }
+  if (lane == 0) p.lse[row] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+}
+
 template <int DP, int DVP>
 static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
-  const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
-  const dim3 grid((unsigned)((int64_t)n_qt * p.Hq * p.B));
+  const int64_t tiles = (int64_t)prefill_group_tiles(p.Q, p.group) * p.Hkv * p.B;
+  const dim3 grid((unsigned)(tiles * p.n_split));
   Params arg = p;
   void* args[] = {&arg};
   const void* const kernels[8] = {
@@ -465,7 +607,12 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   };
   const int exact = p.D == DP && p.Dv == DVP;
   const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
-  return hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
+  if (e != hipSuccess || p.n_split <= 1) return e;
+  const dim3 cgrid((unsigned)(tiles * kPrefillBM / 4));
+  const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true>)
+                          : reinterpret_cast<const void*>(&prefill_combine_kernel<false>);
+  return hipLaunchKernel(cfn, cgrid, dim3(256), args, 0, stream);
 }
 
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream) {

@@ -162,8 +162,9 @@ def cpu_baseline(probs, budget_s: float):
 def run_options(args, torch, af, inputs):
     """attn_fwd_ex / attn_fwd_paged options on the step's two shapes, each call
     timed alone: fp16 storage (causal prefill, decode), the non-causal mode
-    (bf16 prefill, every key legal for every row), and a paged K/V cache
-    (pages of 256 keys for the prefill, 128 for the decode, in random order)."""
+    (bf16 prefill, every key legal for every row), a paged K/V cache (pages of
+    256 keys for the prefill, 128 for the decode, in random order), and two
+    chunked-prefill shapes (short query runs against a long cache)."""
     import dataclasses
     c3, c5 = inputs.config(3), inputs.config(5)
     cases = [
@@ -173,6 +174,12 @@ def run_options(args, torch, af, inputs):
     ]
     cases += [("prefill_paged", dataclasses.replace(c3, name="c3_paged256_prefill")),
               ("decode_paged", dataclasses.replace(c5, name="c5_paged128_decode"))]
+    # Chunked prefill against a long cache, with the step's head layout: a
+    # 64-row chunk (packed tiles of 4 heads, K/V range split 8 ways; K/V bytes
+    # bound it) and a 512-row chunk at batch 1 (per-head tiles split 4 ways).
+    cases += [("prefill_chunk64", inputs.Workload("chunk64_ctx16k_b4_prefill", 4, 32, 8, 64, 16384, 128, 128)),
+              ("prefill_chunk512", inputs.Workload("chunk512_ctx32k_b1_prefill", 1, 32, 8, 512, 32768, 128, 128))]
+    hbm_bound = {"prefill_chunk64"}
     pages = {"prefill_paged": 256, "decode_paged": 128}
     stream = torch.cuda.current_stream()
     parts = {}
@@ -190,7 +197,7 @@ def run_options(args, torch, af, inputs):
         ev[args.steps].record(stream)
         torch.cuda.synchronize()
         t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])) * 1e-3
-        if tag.startswith("prefill"):
+        if tag.startswith("prefill") and tag not in hbm_bound:
             achieved, peak, unit, bound = pr.flops / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = pr.kv_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
@@ -199,7 +206,8 @@ def run_options(args, torch, af, inputs):
         log(f"[bench] {tag}: {1e6 * t:.1f} us/call, {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of peak")
         del pr
         torch.cuda.empty_cache()
-    print(json.dumps({"metric": "options: fp16 storage, non-causal mode, paged K/V cache, % of roofline",
+    print(json.dumps({"metric": "options: fp16 storage, non-causal mode, paged K/V cache, chunked prefill, "
+                                "% of roofline",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic: seeded N(0,1) rounded to the storage type (Philox-4x32-10, seed 1234)",
                       "calls": parts, "kernel_digest": kernel_digest()}), flush=True)

@@ -136,8 +136,13 @@ const char* attn_fwd_strerror(int status);
  * one partial softmax state per group piece; partial_slots bounds the
  * pieces (B*Hkv + split_workers) and workspace_bytes is the scratch the
  * decode path takes from the pool for them (partial_slots * g*Q rows *
- * (Dv + 2) floats).  Returns the status attn_fwd would return for an
- * argument check.
+ * (Dv + 2) floats).  On the prefill path split_workers is the number of
+ * pieces each 128-row tile's key range is cut into (1: none; more when the
+ * tiles alone would leave most of the GPU idle), partial_slots the
+ * (tile, piece) pairs and workspace_bytes their partial states
+ * (partial_slots * 128 rows * (Dv + 2) floats); the fp32 path never
+ * splits.  Returns the status attn_fwd would return for an argument
+ * check.
  */
 typedef struct attn_fwd_plan_t {
   int path;

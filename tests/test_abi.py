@@ -152,3 +152,35 @@ def test_plan_selects_paths():
     assert af.attn_fwd_plan(1, 8, 2, 1, 0, 64, 64)["split_workers"] == 0
     with pytest.raises(af.AttnError):
         af.attn_fwd_plan(1, 8, 3, 1, 10, 64, 64)
+
+
+def test_plan_prefill_splits(monkeypatch):
+    monkeypatch.delenv("ATTN_FWD_PREFILL_SPLITS", raising=False)
+    # 512 tiles fill the GPU: no split.
+    p = af.attn_fwd_plan(4, 32, 8, 4096, 4096, 128, 128)
+    assert (p["split_workers"], p["partial_slots"], p["workspace_bytes"]) == (1, 0, 0)
+    # 32 packed tiles (16 rows of 8 heads each) over 16384 keys (256 blocks):
+    # pieces of at least 32 blocks, so 8 of them (not the 16 that fill 512).
+    p = af.attn_fwd_plan(4, 64, 8, 16, 16384, 128, 128)
+    assert p["path"] == af.PATH_PREFILL and p["split_workers"] == 8
+    assert p["partial_slots"] == 32 * 8 and p["workspace_bytes"] == 256 * 128 * 130 * 4
+    # 128 per-head tiles: 4 pieces fill 512 workgroups.
+    assert af.attn_fwd_plan(1, 32, 8, 512, 32768, 128, 128)["split_workers"] == 4
+    # 4 tiles of 33 blocks: two pieces of at least 16.
+    assert af.attn_fwd_plan(2, 8, 2, 9, 2053, 128, 128)["split_workers"] == 2
+    assert af.attn_fwd_plan(2, 8, 2, 9, 1984, 128, 128)["split_workers"] == 1   # 31 blocks
+    # 4 tiles: 32-block pieces leave most CUs idle, so 16-block ones (8).
+    assert af.attn_fwd_plan(1, 8, 2, 48, 8192, 128, 128)["split_workers"] == 8
+    assert af.attn_fwd_plan(2, 8, 2, 9, 4096, 128, 128)["split_workers"] == 4
+    assert af.attn_fwd_plan(1, 8, 2, 256, 1024, 64, 64)["split_workers"] == 1
+    assert af.attn_fwd_plan(1, 4, 2, 65, 511, 64, 64)["split_workers"] == 1
+    assert af.attn_fwd_plan(1, 4, 2, 65, 0, 64, 64)["split_workers"] == 1
+    # At most 32 pieces; the override is clamped the same way.
+    assert af.attn_fwd_plan(1, 1, 1, 128, 1 << 20, 64, 64)["split_workers"] == 32
+    monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "7")
+    p = af.attn_fwd_plan(1, 4, 2, 65, 100, 64, 96)
+    # 130 packed rows per group: 2 tiles, 2 groups.
+    assert p["split_workers"] == 7 and p["partial_slots"] == 4 * 7 and p["workspace_bytes"] == 28 * 128 * 98 * 4
+    monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "1000")
+    assert af.attn_fwd_plan(1, 4, 2, 65, 100, 64, 64)["split_workers"] == 32
+    # The fp32 path is never split (it has no plan of its own: D, Dv checks only).

@@ -73,6 +73,9 @@ CASES = [
     (2, 4, 2, 300, 768, 64, 64, 256, 0, "f16", True, [768, 500]),
     (2, 8, 2, 256, 512, 128, 128, 128, 64, "bf16", True, [512, 400]),
     (2, 8, 2, 128, 256, 80, 96, 64, 0, "bf16", False, [256, 0]),
+    (2, 16, 2, 60, 1024, 128, 128, 128, 0, "bf16", True, [1024, 317]),   # packed tiles across heads
+    (3, 8, 2, 33, 512, 64, 64, 64, 31, "f16", True, [512, 0, 200]),
+    (2, 32, 4, 100, 768, 128, 128, 256, 0, "bf16", False, [768, 129]),
 ]
 
 

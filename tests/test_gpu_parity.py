@@ -75,6 +75,59 @@ def test_short_query_runs(orc, shape, causal):
         _check(w, window=17, orc=orc, tag=" W=17")
 
 
+# Mid-size query runs (g*Q > 32, Q < 128, g > 1) on the prefill kernel with
+# packed tiles: one tile holds rows of several query heads of a group, and a
+# tile may start or end inside a head (Q not dividing 128).
+MID_Q = [
+    (2, 8, 2, 9, 2053, 128, 128),     # 36 rows: one tile, 4 heads
+    (3, 4, 1, 33, 700, 128, 128),     # 132 rows: a 4-row second tile
+    (2, 16, 2, 60, 1500, 64, 64),     # 480 rows: tiles straddle heads
+    (1, 32, 4, 127, 300, 80, 96),     # 1016 rows, D != Dv
+    (2, 64, 8, 100, 1200, 128, 128),  # 800 rows per group
+    (2, 6, 3, 64, 130, 16, 32),       # two heads fill one tile exactly
+    (1, 8, 2, 48, 8192, 128, 128),    # 4 tiles over 128 blocks: split 4 ways
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", MID_Q, ids=lambda s: "x".join(map(str, s)))
+def test_mid_query_runs_packed(orc, shape, dtype, causal):
+    B = shape[0]
+    sl = np.linspace(0, shape[4], B).astype(np.int32) if B > 2 else np.array([shape[4], 5], np.int32)[:B]
+    w = inputs.Workload("mid_q", *shape, dtype=dtype, seqlens=sl, causal=causal)
+    assert af.attn_fwd_plan(*shape)["path"] == af.PATH_PREFILL
+    _check(w, orc=orc)
+    if causal:
+        _check(w, window=17, orc=orc, tag=" W=17")
+
+
+# Split-KV prefill with the piece count forced (ATTN_FWD_PREFILL_SPLITS):
+# uneven pieces, more pieces than a tile has blocks (empty pieces), empty
+# sequences, windows, packed and per-head tiles, both element types.
+SPLIT_SHAPES = [
+    (2, 8, 2, 200, 700, 128, 128),    # per-head tiles, a 72-row tail tile
+    (2, 16, 2, 60, 1500, 64, 64),     # packed tiles across heads
+    (3, 4, 2, 130, 333, 80, 96),      # D != Dv, padded widths
+    (1, 4, 4, 64, 4100, 64, 128),     # MHA, one tile per head, long keys
+]
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7, 32])
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_forced_splits(orc, shape, splits, monkeypatch):
+    monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", str(splits))
+    assert af.attn_fwd_plan(*shape)["split_workers"] == splits
+    B = shape[0]
+    sl = np.array([shape[4], 0, shape[4] // 3][:B], np.int32)
+    dtype = "f16" if splits == 3 else "bf16"
+    w = inputs.Workload("split", *shape, dtype=dtype, seqlens=sl)
+    _check(w, orc=orc, tag=f" splits={splits}")
+    _check(w, window=100, orc=orc, tag=f" splits={splits} W=100")
+    w = inputs.Workload("split_nc", *shape, dtype=dtype, seqlens=sl, causal=False)
+    _check(w, orc=orc, tag=f" splits={splits}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_noncausal_shape_matrix(orc, shape, dtype):
