@@ -544,9 +544,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 // n_split partial states in split order (the merge of two online-softmax
 // states: rescale both to the larger max, add sums and accumulators), then
 // normalises and writes O and the LSE.  Lane l owns channels 2l, 2l + 1.
+// The pieces are taken eight at a time, all their loads issued together, and
+// folded into a running (M, L, o); a piece with m = -inf has no acc (never
+// written) and is skipped.
 template <bool F16>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
   using E = Elem<F16>;
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int per_grp = prefill_group_tiles(p.Q, p.group);
@@ -559,28 +563,44 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
   if (r >= tile.n_rows) return;
   const int hh = r / p.Q, q = r - hh * p.Q;
   const int64_t row = ((int64_t)tile.b * p.Hq + tile.h_base + hh) * p.Q + q;
-  auto slot_of = [&](int s) { return ((int64_t)(grp * p.n_split + s) * per_grp + rem) * kPrefillBM + r_local; };
-
-  float mx = -INFINITY;
-  for (int s = 0; s < p.n_split; ++s) mx = fmaxf(mx, p.ws_m[slot_of(s)]);
-  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  // Slot of piece s: ((grp * n_split + s) * per_grp + rem) * 128 + r_local.
+  const int64_t slot0 = ((int64_t)grp * p.n_split * per_grp + rem) * kPrefillBM + r_local;
+  const int64_t slot_step = (int64_t)per_grp * kPrefillBM;
   const int dv = 2 * lane;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < p.n_split; ++s) {
-      const int64_t slot = slot_of(s);
-      const float ms = p.ws_m[slot];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - mx);
-      l += p.ws_l[slot] * w;
-      if (dv < p.Dv) {
-        const float2 a = *reinterpret_cast<const float2*>(p.ws_acc + slot * p.Dv + dv);
-        o0 += a.x * w;
-        o1 += a.y * w;
-      }
+  const bool has_dv = dv < p.Dv;
+
+  float mx = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < p.n_split; s0 += U) {
+    float ms[U], ls[U];
+    float2 a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t slot = slot0 + (int64_t)(s0 + u) * slot_step;
+      const bool in = s0 + u < p.n_split;
+      ms[u] = in ? p.ws_m[slot] : -INFINITY;
+      ls[u] = in ? p.ws_l[slot] : 0.f;
+      a[u] = (in && has_dv) ? *reinterpret_cast<const float2*>(p.ws_acc + slot * p.Dv + dv) : float2{0.f, 0.f};
     }
+    float mn = mx;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mn = fmaxf(mn, ms[u]);
+    if (mn == -INFINITY) continue;
+    const float alpha = exp2f(mx - mn);  // 0 while nothing is merged yet (mx = -inf)
+    l *= alpha;
+    o0 *= alpha;
+    o1 *= alpha;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ms[u] == -INFINITY) continue;
+      const float w = exp2f(ms[u] - mn);
+      l += ls[u] * w;
+      o0 += a[u].x * w;
+      o1 += a[u].y * w;
+    }
+    mx = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (dv < p.Dv) {
+  if (has_dv) {
     ushort2 ov;
     ov.x = E::cvt(o0 * inv);
     ov.y = E::cvt(o1 * inv);
