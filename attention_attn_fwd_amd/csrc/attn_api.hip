@@ -55,7 +55,9 @@ int launch_status(hipError_t e) {
   return ATTN_ERR_HIP;
 }
 
-bool supported_width(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+// Head widths: multiples of 16 up to 256 on the 16-bit MFMA kernels (above
+// 128 the 8-wave prefill form), up to 128 on the fp32 kernel.
+bool supported_width(int d, bool mfma) { return d >= 16 && d <= (mfma ? 256 : 128) && d % 16 == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -99,11 +101,24 @@ int prefill_splits(int B, int Hkv, int Q, int group, int K) {
   }
   const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
   constexpr int64_t kSlots = 512, kCUs = 256;
-  if (tiles >= kSlots) return 1;
   const int64_t blocks = ((int64_t)K + kPrefillBN - 1) / kPrefillBN;
-  int64_t s = std::min((kSlots + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocks);
-  if (tiles * s < kCUs) s = std::max(s, std::min((kCUs + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocksIdle));
+  int64_t s = 1;
+  if (tiles < kSlots) {
+    s = std::min((kSlots + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocks);
+    if (tiles * s < kCUs) s = std::max(s, std::min((kCUs + tiles - 1) / tiles, blocks / kPrefillMinSplitBlocksIdle));
+  }
+  // Lean tiles (at most 64 rows, as in decode with wide heads): their partial
+  // states are small next to a piece's K/V, and with lengths that vary one
+  // long sequence would otherwise hold a single workgroup for its whole range.
+  const int64_t rows = std::min<int64_t>(kPrefillBM, prefill_packed(Q, group) ? (int64_t)group * Q : Q);
+  if (rows <= 64) s = std::max(s, blocks / kPrefillMinSplitBlocks);
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, kPrefillMaxSplits));
+}
+
+// Blocks per piece when the longest key range (K) is cut into `splits`.
+int prefill_split_blocks(int K, int splits) {
+  const int blocks = (K + kPrefillBN - 1) / kPrefillBN;
+  return (blocks + splits - 1) / splits;
 }
 
 // Checks shared by both entry points; fills the plan.
@@ -115,7 +130,7 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Hq * Q == 0) return ATTN_OK;
-  if (!supported_width(D) || !supported_width(Dv)) return ATTN_ERR_UNSUPPORTED;
+  if (!supported_width(D, bf16) || !supported_width(Dv, bf16)) return ATTN_ERR_UNSUPPORTED;
   // Byte offsets inside one (batch, head) slice are 32-bit in the kernels, and
   // the buffer loads read a padding channel as zero by giving it an offset
   // of 2^31, past the end of any slice below that size.
@@ -124,7 +139,7 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
       (int64_t)K * Dv * 2 >= lim)
     return ATTN_ERR_UNSUPPORTED;
   const int group = Hq / Hkv;
-  if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows) {
+  if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows && D <= 128 && Dv <= 128) {
     plan->path = 2;
     plan->split_workers = split_workers(B, Hkv, K, D, Dv, group * Q);
     plan->partial_slots = plan->split_workers > 0 ? B * Hkv + plan->split_workers : 0;
@@ -137,7 +152,11 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
     // times at most kPrefillMaxSplits pieces.
     if ((int64_t)((Q + bm - 1) / bm) * Hq * B > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
     if (bf16) {
-      const int ns = prefill_splits(B, Hkv, Q, group, K);
+      // Pieces of a fixed number of blocks: the requested count rounded to
+      // what whole pieces of ceil(blocks / count) blocks need.
+      const int want = prefill_splits(B, Hkv, Q, group, K);
+      const int blocks = (K + kPrefillBN - 1) / kPrefillBN;
+      const int ns = want > 1 ? (blocks + prefill_split_blocks(K, want) - 1) / prefill_split_blocks(K, want) : 1;
       plan->split_workers = ns;
       if (ns > 1) {
         const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
@@ -205,6 +224,7 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   int64_t parts;
   if (plan.path == 1) {
     p.n_split = plan.split_workers;
+    p.split_blocks = prefill_split_blocks(K, p.n_split);
     parts = (int64_t)plan.partial_slots * kPrefillBM;
   } else {
     p.n_workers = plan.split_workers;
@@ -274,7 +294,8 @@ const char* attn_fwd_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported size (D and Dv must be multiples of 16 in [16, 128])";
+    case ATTN_ERR_UNSUPPORTED:
+      return "unsupported size (D and Dv must be multiples of 16 in [16, 256], [16, 128] in fp32)";
     case ATTN_ERR_OOM: return "scratch allocation failed";
     case ATTN_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";

@@ -32,12 +32,14 @@ __host__ __device__ inline int prefill_group_tiles(int Q, int group) {
   return prefill_packed(Q, group) ? (group * Q + kPrefillBM - 1) / kPrefillBM : group * n_qt;
 }
 // Split-KV prefill: when the tiles alone leave most workgroup slots of the
-// chip idle (few long sequences), each tile's key range is cut into n_split
-// contiguous pieces of whole blocks, processed by separate workgroups that
-// write fp32 partial states; a combine pass merges them.  At most
-// kPrefillMaxSplits pieces, each at least kPrefillMinSplitBlocks blocks
-// (kPrefillMinSplitBlocksIdle while the pieces would not give every CU a
-// workgroup).
+// chip idle (few long sequences), or hold so few rows that one long sequence
+// would keep a single workgroup busy long after the rest (decode-like tiles
+// over lengths that vary), each tile's key range is cut into pieces of a
+// fixed number of blocks, processed by separate workgroups that write fp32
+// partial states; a combine pass merges them.  A tile whose range is short
+// leaves its later pieces empty.  At most kPrefillMaxSplits pieces, each at
+// least kPrefillMinSplitBlocks blocks (kPrefillMinSplitBlocksIdle while the
+// pieces would not give every CU a workgroup).
 constexpr int kPrefillMaxSplits = 32;
 constexpr int kPrefillMinSplitBlocks = 32;
 constexpr int kPrefillMinSplitBlocksIdle = 16;
@@ -74,13 +76,14 @@ struct Params {
   float scale;             // raw scale (fp32 path)
   // Split-KV scratch.  Decode: one partial per (slot, row), slot = group +
   // worker.  Prefill: one per (part, tile row), part = (group * n_split +
-  // split) * tiles per group + tile, tile row in [0, 128).
+  // piece) * tiles per group + tile, tile row in [0, 128).
   float* ws_m;             // [slots][rows]  running max, log2 units
   float* ws_l;             // [slots][rows]  sum of 2^(s*c - m)
   float* ws_acc;           // [slots][rows][Dv] unnormalised P.V
   int n_workers;           // workgroups of the split pass (0: no keys at all)
   int rows;                // group * Q
   int n_split;             // prefill: key-range pieces per tile (1: no split)
+  int split_blocks;        // prefill: 64-key blocks per piece (piece s starts s * split_blocks into the tile's range)
   // Paged K/V cache (block_table null: contiguous k [B,Hkv,K,D], v [B,Hkv,K,Dv]).
   // Otherwise k [num_pages,Hkv,2^page_shift,D], v [num_pages,Hkv,2^page_shift,Dv]
   // and keys [j << page_shift, (j + 1) << page_shift) of sequence b are in page
@@ -101,7 +104,7 @@ hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
 constexpr int kMinPageShift = 6;
 
 // Padded widths the kernels are instantiated for.
-inline int pad_width(int d) { return d <= 64 ? 64 : 128; }
+inline int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
 
 // Row q of sequence b sits at absolute position q + row_delta: K_b - Q
 // (bottom-right alignment), or, without the causal limit, far enough past
@@ -367,11 +370,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // LDS tiles of rows of NCH 16-byte chunks are stored XOR-swizzled: chunk c of
-// row r sits at chunk position c ^ swz(r).  K tiles use swz(r) = r % NCH so the
-// 16 rows of a 16-byte MFMA-fragment read hit distinct banks; V tiles use
-// swz(r) = 2r % NCH so the 4-row, 32-byte pieces of a transposed read do.
+// row r sits at chunk position c ^ swz(r).  K tiles use swz(r) = r % min(NCH,
+// 16) so the 16 rows of a 16-byte MFMA-fragment read hit distinct banks; V
+// tiles use swz(r) = 2r % NCH so the 4-row, 32-byte pieces of a transposed
+// read do.
 template <int NCH>
-__device__ __forceinline__ int swz_k(int row) { return row & (NCH - 1); }
+__device__ __forceinline__ int swz_k(int row) { return row & ((NCH < 16 ? NCH : 16) - 1); }
 template <int NCH>
 __device__ __forceinline__ int swz_v(int row) { return (2 * row) & (NCH - 1); }
 

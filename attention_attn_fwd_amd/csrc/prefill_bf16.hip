@@ -45,8 +45,18 @@
 
 namespace attn {
 
-template <int DP, int DVP>
+// Padded widths DP, DVP; NW waves per workgroup, each owning NT 16-row MFMA
+// tiles of the 128-row tile (NW * NT * 16 = 128).  Heads up to 128 wide use
+// 4 waves of 32 rows, two workgroups per CU; wider heads use 8 waves of 16
+// rows (half the per-wave registers: the Q fragments and accumulators of a
+// 256-wide head), one workgroup per CU, so the two waves on a SIMD still
+// overlap one's softmax with the other's products.
+// LDS ring: K of stage 0, K of stage 1, V of stage 0, V of stage 1, so every
+// read offset that depends on the stage or the key tile fits the 16-bit
+// immediate of a ds_read.
+template <int DP, int DVP, int NW>
 struct PrefillShape {
+  static constexpr int NT = kPrefillBM / (16 * NW);  // 16-row MFMA tiles per wave
   static constexpr int KS = DP / 32;        // 32-deep k-steps of Q.K
   static constexpr int JV = DVP / 16;       // 16-wide dv tiles of O^T
   static constexpr int KCH = DP / 8;        // 16-byte chunks per K row
@@ -55,14 +65,20 @@ struct PrefillShape {
   static constexpr int VROWB = DVP * 2;
   static constexpr int K_TILE = kPrefillBN * KROWB;
   static constexpr int V_TILE = kPrefillBN * VROWB;
-  static constexpr int STAGE = K_TILE + V_TILE;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int K_LOADS = K_TILE / 4096;  // 16-byte loads per thread per block
-  static constexpr int V_LOADS = V_TILE / 4096;
-  static constexpr int K_ROWS_PER_LOAD = 4096 / KROWB;  // tile rows one 4 KiB load round covers
-  static constexpr int V_ROWS_PER_LOAD = 4096 / VROWB;
-  static_assert(K_TILE % 4096 == 0 && V_TILE % 4096 == 0, "load split");
-  static_assert(LDS <= 65536, "ds_read immediate offsets cover the ring");
+  static constexpr int V_BASE = 2 * K_TILE;
+  static constexpr int LDS = 2 * (K_TILE + V_TILE);
+  static constexpr int ROUND = NW * 1024;   // bytes one wave-wide 16-byte load round of the workgroup covers
+  static constexpr int K_LOADS = K_TILE / ROUND;  // 16-byte loads per thread per block
+  static constexpr int V_LOADS = V_TILE / ROUND;
+  static constexpr int K_ROWS_PER_LOAD = ROUND / KROWB;  // tile rows one load round covers
+  static constexpr int V_ROWS_PER_LOAD = ROUND / VROWB;
+  static_assert(NT * 16 * NW == kPrefillBM && (NT == 1 || NT == 2), "tile geometry");
+  static_assert(K_TILE % ROUND == 0 && V_TILE % ROUND == 0, "load split");
+  // A load round covers whole swizzle periods, so a lane's chunk is the same
+  // in every round (periods: 16 rows or fewer for K, VCH / 2 for V).
+  static_assert(K_ROWS_PER_LOAD % (KCH < 16 ? KCH : 16) == 0 && V_ROWS_PER_LOAD % (VCH / 2) == 0, "swizzle");
+  static_assert(K_TILE + 3 * 16 * KROWB < 65536 && V_TILE + 48 * VROWB < 65536, "ds_read immediates");
+  static_assert(LDS <= 160 * 1024, "LDS of a CU");
 };
 
 // A tile: rows [r0, r0 + 128) of the row list of one (batch, kv-head) group
@@ -95,7 +111,7 @@ __device__ __forceinline__ PrefillTile prefill_tile_of(const Params& p, int grp,
   return t;
 }
 
-// Block index -> tile.  A virtual group is a (group, split) pair.  When the
+// Block index -> tile.  A virtual group is a (piece, group) pair.  When the
 // virtual groups divide evenly over the 8 XCDs (workgroup i runs on XCD
 // i % 8), each XCD gets whole virtual groups and finishes one (all its
 // tiles, heaviest first) before the next, so the workgroups resident on an
@@ -115,10 +131,15 @@ __device__ __forceinline__ PrefillTile prefill_tile(const Params& p) {
     rem = x / vgroups;
     vg = x - rem * vgroups;
   }
-  const int grp = vg / p.n_split;
+  // Split-major: virtual group vg is piece vg / groups of group vg % groups,
+  // so an XCD gets every piece of its groups (pieces late in a range are
+  // often empty; dealing pieces to XCDs would leave the XCDs that got the
+  // first pieces with most of the work).
+  const int groups = p.B * p.Hkv;
+  const int split = vg / groups, grp = vg - split * groups;
   PrefillTile t = prefill_tile_of(p, grp, rem);
-  t.split = vg - grp * p.n_split;
-  t.part = vg * per_grp + rem;
+  t.split = split;
+  t.part = (grp * p.n_split + split) * per_grp + rem;  // a row's pieces lie 128 rows apart
   return t;
 }
 
@@ -139,9 +160,11 @@ __device__ __forceinline__ void row_q_range(int r0, int r1, int Q, int* qlo, int
 // no channel is padding (the common case); otherwise padded channels read zero.
 // F16: the 16-bit inputs and output are IEEE binary16 instead of bf16.
 // PAGED: K and V live in a paged cache (Params::block_table).
-template <int DP, int DVP, bool EXACT, bool F16, bool PAGED>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
-  using S = PrefillShape<DP, DVP>;
+template <int DP, int DVP, int NW, bool EXACT, bool F16, bool PAGED>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p) {
+  using S = PrefillShape<DP, DVP, NW>;
+  constexpr int NT = S::NT;
+  constexpr int ROWS_W = 16 * NT;  // rows per wave
   using E = Elem<F16>;
   constexpr int BN = kPrefillBN;
   const int D = EXACT ? DP : p.D;
@@ -167,27 +190,27 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   const int kv_lo = W > 0 ? max(0, tq_lo + delta - W + 1) : 0;
   int jb0 = kv_lo / BN;
   int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
-  if (p.n_split > 1) {  // this workgroup's piece: blocks split as evenly as they go
-    const int nb = jb1 - jb0, s0 = jb0;
-    jb0 = s0 + (int)((int64_t)nb * tile.split / p.n_split);
-    jb1 = s0 + (int)((int64_t)nb * (tile.split + 1) / p.n_split);
+  if (p.n_split > 1) {  // this workgroup's piece: split_blocks blocks, or what is left of them
+    const int64_t s0 = (int64_t)jb0 + (int64_t)tile.split * p.split_blocks;
+    jb0 = (int)min((int64_t)jb1, s0);
+    jb1 = (int)min((int64_t)jb1, s0 + p.split_blocks);
   }
 
   // Wave-level (scalar) row range and the positions its rows span.
-  const int rw0 = tile.r0 + wave * kPrefillRowsPerWave;
+  const int rw0 = tile.r0 + wave * ROWS_W;
   const bool wave_has_rows = rw0 < tile.n_rows;
   int qw_lo = 0, qw_hi = 0;
-  if (wave_has_rows) row_q_range(rw0, min(rw0 + kPrefillRowsPerWave, tile.n_rows) - 1, Q, &qw_lo, &qw_hi);
+  if (wave_has_rows) row_q_range(rw0, min(rw0 + ROWS_W, tile.n_rows) - 1, Q, &qw_lo, &qw_hi);
   const int pw_first = qw_lo + delta, pw_last = qw_hi + delta;
   const float c = p.scale_log2;
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
-  // This lane's two rows (one per 16-row MFMA tile): query row q_row[t] of
-  // head h_base + hh_row[t]; row_ok[t] false past the row list.
-  int q_row[2], hh_row[2];
-  bool row_ok[2];
+  // This lane's rows (one per 16-row MFMA tile): query row q_row[t] of head
+  // h_base + hh_row[t]; row_ok[t] false past the row list.
+  int q_row[NT], hh_row[NT];
+  bool row_ok[NT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
     const int r = rw0 + 16 * t + l16;
     row_ok[t] = r < tile.n_rows;
     hh_row[t] = r / Q;
@@ -196,12 +219,29 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   auto row_index = [&](int t) {  // flat (b, head, q) row of O and LSE
     return ((int64_t)b * p.Hq + tile.h_base + hh_row[t]) * Q + q_row[t];
   };
+  // Partial-state slot of this lane's row t in a split pass.
+  auto part_slot = [&](int t) { return (int64_t)tile.part * kPrefillBM + (rw0 - tile.r0) + 16 * t + l16; };
+
+  // An empty piece of a split pass (past the end of this tile's range): its
+  // rows saw no key here.  The condition is uniform over the workgroup.
+  if (p.n_split > 1 && jb0 >= jb1) {
+    if (wave_has_rows && g4 == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (row_ok[t]) {
+          p.ws_m[part_slot(t)] = -INFINITY;
+          p.ws_l[part_slot(t)] = 0.f;
+        }
+      }
+    }
+    return;
+  }
 
   // Q fragments (B operand of S^T = K Q^T): lane holds row l16 of the tile,
   // channels 32s + 8*g4 .. +7.
-  bf16x8 qf[2][S::KS];
+  bf16x8 qf[NT][S::KS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + row_index(t) * D;
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
@@ -214,24 +254,24 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // Q is in registers before any direct load is issued.
   wait_vmcnt<0>();
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) launder(qf[t][s]);
 
-  // Direct loads.  Load round i of wave w fills tile bytes [(4i + w) KiB,
+  // Direct loads.  Load round i of wave w fills tile bytes [(NW*i + w) KiB,
   // +1 KiB); lane l's 16 bytes land at position l of that KiB, so the lane
   // fetches the global chunk the swizzle puts there.  A round covers a whole
   // number of swizzle periods of rows, so the chunk a lane fetches is the same
   // in every round and its global offset advances by a fixed step.
-  auto lane_off = [&](int rowb, int nch, bool is_v, int width) -> uint32_t {
+  auto lane_off = [&](int rowb, bool is_v, int width) -> uint32_t {
     const int off = wave * 1024 + 16 * lane;
     const int row = off / rowb, pos = (off % rowb) >> 4;
-    const int ch = pos ^ (is_v ? ((2 * row) & (nch - 1)) : (row & (nch - 1)));
+    const int ch = pos ^ (is_v ? swz_v<S::VCH>(row) : swz_k<S::KCH>(row));
     if (EXACT) return (uint32_t)(row * width + ch * 8) * 2;
     return ch < width / 8 ? (uint32_t)(row * width + ch * 8) * 2 : kOutOfRange;
   };
-  const uint32_t koff = lane_off(S::KROWB, S::KCH, false, D);
-  const uint32_t voff = lane_off(S::VROWB, S::VCH, true, Dv);
+  const uint32_t koff = lane_off(S::KROWB, false, D);
+  const uint32_t voff = lane_off(S::VROWB, true, Dv);
   const uint32_t kstep = (uint32_t)(S::K_ROWS_PER_LOAD * D * 2);
   const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv * 2);
   const uint32_t lds0 = lds_offset(ring);
@@ -243,15 +283,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
     const rsrc_t rk = slice_rsrc(sp.k, rows_left * D * 2);
     const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv * 2);
-    const uint32_t base = lds0 + stg * S::STAGE + wave * 1024;
+    const uint32_t kbase = lds0 + stg * S::K_TILE + wave * 1024;
+    const uint32_t vbase = lds0 + S::V_BASE + stg * S::V_TILE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, base + i * 4096, koff + i * kstep);
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, kbase + i * S::ROUND, koff + i * kstep);
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, base + S::K_TILE + i * 4096, voff + i * vstep);
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, vbase + i * S::ROUND, voff + i * vstep);
   };
 
   // Per-lane LDS read offsets (stage 0).  K fragment of k-step s, key tile i:
-  // row 16i + l16, chunk (4s + g4) ^ swz_k(row); swz_k(row) = l16 % KCH for
+  // row 16i + l16, chunk (4s + g4) ^ swz_k(row); swz_k(row) = swz_k(l16) for
   // every i.  V^T fragment of dv tile j: rows 32kk + 4*g4 + l16/4 (+16), chunk
   // (2j + (l16 & 3)/2) ^ swz_v(row), half (l16 & 1); swz_v is the same for
   // every kk and for the +16 row.
@@ -263,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     const int vrow = 4 * g4 + (l16 >> 2);
 #pragma unroll
     for (int j = 0; j < S::JV; ++j)
-      va[j] = lds0 + S::K_TILE + vrow * S::VROWB + (((2 * j + ((l16 & 3) >> 1)) ^ swz_v<S::VCH>(vrow)) << 4) +
+      va[j] = lds0 + S::V_BASE + vrow * S::VROWB + (((2 * j + ((l16 & 3) >> 1)) ^ swz_v<S::VCH>(vrow)) << 4) +
               (l16 & 1) * 8;
   }
 
@@ -278,11 +319,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     return (kb0 + BN - 1 <= pw_first) && (kb0 + BN <= Kb) && (W <= 0 || kb0 >= pw_last - W + 1);
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 acc[S::JV][2];
+  float m_run[NT], l_run[NT];
+  f32x4 acc[S::JV][NT];
 #pragma unroll
-  for (int j = 0; j < S::JV; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < S::JV; ++j) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Initial S^T accumulator of a block that straddles the causal diagonal, a
   // window edge or the sequence end: 0 for a legal key, -inf otherwise, so the
@@ -290,9 +335,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // r) is legal for query position pq iff lo <= x <= hi, with hi from
   // causality and K_b and lo from the window: one unsigned compare against an
   // immediate x per element.
-  auto mask_bias = [&](int kb0, f32x4 (&s)[4][2]) {
+  auto mask_bias = [&](int kb0, f32x4 (&s)[4][NT]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int rel = q_row[t] + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
       const int hi = min(rel, Kb - kb0 - 4 * g4 - 1);
       const int lo = W > 0 ? max(rel - W + 1, 0) : 0;
@@ -313,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // factor c is positive, so -inf * c stays -inf).
   // Column max over the block in log2 units (-inf: no legal key; c > 0 keeps
   // -inf * c at -inf): per-lane v_max3 chain, then the four lane groups.
-  auto block_max = [&](const f32x4 (&s)[4][2], int t) {
+  auto block_max = [&](const f32x4 (&s)[4][NT], int t) {
     float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
     mx = max3f(mx, s[0][t][3], s[1][t][0]);
     mx = max3f(mx, s[1][t][1], s[1][t][2]);
@@ -332,9 +377,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // stays; no block max is computed.  Otherwise, or while a row has no
   // reference yet, the column max moves the reference, the accumulators are
   // rescaled and the weights recomputed (rare: a few blocks per row).
-  auto softmax = [&](const f32x4 (&s)[4][2], bf16x8 (&pf)[2][2]) {
-    f32x4 e[4][2];
-    float rs[2];
+  auto softmax = [&](const f32x4 (&s)[4][NT], bf16x8 (&pf)[NT][2]) {
+    f32x4 e[4][NT];
+    float rs[NT];
     auto weights = [&](int t) {
       const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
       float sum = 0.f;
@@ -348,14 +393,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       }
       rs[t] = sum;
     };
-    weights(0);
-    weights(1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) weights(t);
     constexpr float kBound = 256.f;  // 2^kLazyRescale
     static_assert(kLazyRescale == 8.f, "kBound is 2^kLazyRescale");
-    const bool need = !(rs[0] <= kBound) || !(rs[1] <= kBound) || m_run[0] == -INFINITY || m_run[1] == -INFINITY;
+    bool need = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) need = need | !(rs[t] <= kBound) | (m_run[t] == -INFINITY);
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const float mnew = fmaxf(m_run[t], block_max(s, t));
         const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m_run[t] - mnew);
         m_run[t] = mnew;
@@ -366,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       }
     }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       l_run[t] += rs[t];
       pf[t][0] = E::pack(e[0][t], e[1][t]);
       pf[t][1] = E::pack(e[2][t], e[3][t]);
@@ -380,10 +427,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
   // rest (mask_bias).
   auto body = [&](int jb, auto stg_tag, bool full) {
     constexpr int STG = decltype(stg_tag)::value;
-    constexpr uint32_t SOFF = STG * S::STAGE;
+    constexpr uint32_t KOFF = STG * S::K_TILE, VOFF = STG * S::V_TILE;
     {
       const int kb0 = jb * BN;
-      f32x4 s[4][2];
+      f32x4 s[4][NT];
       // S^T = K Q^T.  The K fragments of k-step st + 1 are read while the
       // MFMAs of k-step st run; the fences keep the compiler from hoisting
       // every read of the block (64 registers) ahead of the products.
@@ -392,17 +439,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         bf16x8 ak[2][4];
         if constexpr (!FULL) mask_bias(kb0, s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(ka[0] + SOFF + 16 * i * S::KROWB);
+        for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(ka[0] + KOFF + 16 * i * S::KROWB);
 #pragma unroll
         for (int st = 0; st < S::KS; ++st) {
           if (st + 1 < S::KS) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(ka[st + 1] + SOFF + 16 * i * S::KROWB);
+            for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(ka[st + 1] + KOFF + 16 * i * S::KROWB);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < NT; ++t) {
               const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
               s[i][t] = E::mfma(ak[st & 1][i], qf[t][st], c0);
             }
@@ -414,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       else qk(std::false_type{});
       // V^T fragment of (kk, j): rows 32kk + 4*g4 + l16/4 and 16 below.
       auto read_v = [&](int kk, int j) {
-        const uint32_t lo = va[j] + SOFF + 32 * kk * S::VROWB;
+        const uint32_t lo = va[j] + VOFF + 32 * kk * S::VROWB;
         return concat_bf16x4(lds_read_tr16(lo), lds_read_tr16(lo + 16 * S::VROWB));
       };
       // The first two V fragments are in flight during the softmax.
@@ -422,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
       av[0][0] = read_v(0, 0);
       av[0][1] = read_v(0, 1);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 pf[2][2];
+      bf16x8 pf[NT][2];
       softmax(s, pf);
       __builtin_amdgcn_sched_barrier(0);
       // O^T += V^T P^T over two 32-key halves, two dv tiles per step with the
@@ -440,8 +487,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          acc[j + u][0] = E::mfma(av[n & 1][u], pf[0][kk], acc[j + u][0]);
-          acc[j + u][1] = E::mfma(av[n & 1][u], pf[1][kk], acc[j + u][1]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[j + u][t] = E::mfma(av[n & 1][u], pf[t][kk], acc[j + u][t]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -496,10 +543,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     // Partial state of this piece: (m, l) and the unnormalised acc; a row
     // that saw no legal key gets m = -inf, l = 0 and no acc.
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const float lt = group4_sum(l_run[t]);
       if (row_ok[t]) {
-        const int64_t slot = (int64_t)tile.part * kPrefillBM + (rw0 - tile.r0) + 16 * t + l16;
+        const int64_t slot = part_slot(t);
         if (g4 == 0) {
           p.ws_m[slot] = lt > 0.f ? m_run[t] : -INFINITY;
           p.ws_l[slot] = lt;
@@ -517,7 +564,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
     return;
   }
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NT; ++t) {
     const float lt = group4_sum(l_run[t]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok[t]) {
@@ -543,12 +590,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(Params p) {
 // Combine pass of split-KV prefill: one wave per tile row merges the row's
 // n_split partial states in split order (the merge of two online-softmax
 // states: rescale both to the larger max, add sums and accumulators), then
-// normalises and writes O and the LSE.  Lane l owns channels 2l, 2l + 1.
+// normalises and writes O and the LSE.  Lane l owns channels CPL*l ..
+// CPL*l + CPL - 1 (CPL = 2 up to 128 channels, 4 up to 256).
 // The pieces are taken eight at a time, all their loads issued together, and
 // folded into a running (M, L, o); a piece with m = -inf has no acc (never
 // written) and is skipped.
-template <bool F16>
+template <bool F16, int CPL>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
+  using V = std::conditional_t<CPL == 2, float2, float4>;
   using E = Elem<F16>;
   constexpr int U = 8;
   const int lane = threadIdx.x & 63;
@@ -566,20 +615,20 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
   // Slot of piece s: ((grp * n_split + s) * per_grp + rem) * 128 + r_local.
   const int64_t slot0 = ((int64_t)grp * p.n_split * per_grp + rem) * kPrefillBM + r_local;
   const int64_t slot_step = (int64_t)per_grp * kPrefillBM;
-  const int dv = 2 * lane;
-  const bool has_dv = dv < p.Dv;
+  const int dv = CPL * lane;
+  const bool has_dv = dv < p.Dv;  // Dv is a multiple of 16: all CPL channels or none
 
-  float mx = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  float mx = -INFINITY, l = 0.f, o[CPL] = {};
   for (int s0 = 0; s0 < p.n_split; s0 += U) {
     float ms[U], ls[U];
-    float2 a[U];
+    V a[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t slot = slot0 + (int64_t)(s0 + u) * slot_step;
       const bool in = s0 + u < p.n_split;
       ms[u] = in ? p.ws_m[slot] : -INFINITY;
       ls[u] = in ? p.ws_l[slot] : 0.f;
-      a[u] = (in && has_dv) ? *reinterpret_cast<const float2*>(p.ws_acc + slot * p.Dv + dv) : float2{0.f, 0.f};
+      a[u] = (in && has_dv) ? *reinterpret_cast<const V*>(p.ws_acc + slot * p.Dv + dv) : V{};
     }
     float mn = mx;
 #pragma unroll
@@ -587,60 +636,74 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
     if (mn == -INFINITY) continue;
     const float alpha = exp2f(mx - mn);  // 0 while nothing is merged yet (mx = -inf)
     l *= alpha;
-    o0 *= alpha;
-    o1 *= alpha;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] *= alpha;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ms[u] == -INFINITY) continue;
       const float w = exp2f(ms[u] - mn);
       l += ls[u] * w;
-      o0 += a[u].x * w;
-      o1 += a[u].y * w;
+      const float* av = reinterpret_cast<const float*>(&a[u]);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] += av[c] * w;
     }
     mx = mn;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (has_dv) {
-    ushort2 ov;
-    ov.x = E::cvt(o0 * inv);
-    ov.y = E::cvt(o1 * inv);
-    *reinterpret_cast<ushort2*>(static_cast<uint16_t*>(p.o) + row * p.Dv + dv) = ov;
+    uint16_t* orow = static_cast<uint16_t*>(p.o) + row * p.Dv + dv;
+    if constexpr (CPL == 2) {
+      ushort2 ov;
+      ov.x = E::cvt(o[0] * inv);
+      ov.y = E::cvt(o[1] * inv);
+      *reinterpret_cast<ushort2*>(orow) = ov;
+    } else {
+      ushort4 ov;
+      ov.x = E::cvt(o[0] * inv);
+      ov.y = E::cvt(o[1] * inv);
+      ov.z = E::cvt(o[2] * inv);
+      ov.w = E::cvt(o[3] * inv);
+      *reinterpret_cast<ushort4*>(orow) = ov;
+    }
   }
   if (lane == 0) p.lse[row] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
-template <int DP, int DVP>
+template <int DP, int DVP, int NW>
 static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const int64_t tiles = (int64_t)prefill_group_tiles(p.Q, p.group) * p.Hkv * p.B;
   const dim3 grid((unsigned)(tiles * p.n_split));
   Params arg = p;
   void* args[] = {&arg};
   const void* const kernels[8] = {
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, false, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, false, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, false, true, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, true, true, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, true, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, true, true>),
   };
   const int exact = p.D == DP && p.Dv == DVP;
   const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
-  hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * NW), args, 0, stream);
   if (e != hipSuccess || p.n_split <= 1) return e;
   const dim3 cgrid((unsigned)(tiles * kPrefillBM / 4));
-  const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true>)
-                          : reinterpret_cast<const void*>(&prefill_combine_kernel<false>);
+  constexpr int CPL = DVP <= 128 ? 2 : 4;
+  const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, CPL>)
+                          : reinterpret_cast<const void*>(&prefill_combine_kernel<false, CPL>);
   return hipLaunchKernel(cfn, cgrid, dim3(256), args, 0, stream);
 }
 
+// Heads wider than 128 (padded to 256 on both sides) take the 8-wave form.
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream) {
   const int dp = pad_width(p.D), dvp = pad_width(p.Dv);
-  if (dp == 64 && dvp == 64) return launch_prefill_t<64, 64>(p, stream);
-  if (dp == 64 && dvp == 128) return launch_prefill_t<64, 128>(p, stream);
-  if (dp == 128 && dvp == 64) return launch_prefill_t<128, 64>(p, stream);
-  return launch_prefill_t<128, 128>(p, stream);
+  if (dp > 128 || dvp > 128) return launch_prefill_t<256, 256, 8>(p, stream);
+  if (dp == 64 && dvp == 64) return launch_prefill_t<64, 64, 4>(p, stream);
+  if (dp == 64 && dvp == 128) return launch_prefill_t<64, 128, 4>(p, stream);
+  if (dp == 128 && dvp == 64) return launch_prefill_t<128, 64, 4>(p, stream);
+  return launch_prefill_t<128, 128, 4>(p, stream);
 }
 
 }  // namespace attn

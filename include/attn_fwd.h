@@ -31,9 +31,16 @@
  * Ownership: the caller owns every buffer.  The library keeps no pointer past
  * the call's stream-ordered completion and frees nothing it did not
  * allocate.  Inputs are only read.  o and lse must not alias the inputs.
- * Scratch for the split-KV decode path comes from a library-owned,
- * stream-ordered HIP memory pool (allocated and released on `stream`), so
- * concurrent calls on different streams do not share scratch.
+ * Scratch for the split-KV passes (decode, and prefill when its tiles are
+ * few) comes from a library-owned, stream-ordered HIP memory pool
+ * (allocated and released on `stream`), so concurrent calls on different
+ * streams do not share scratch.
+ *
+ * Head widths: D and Dv up to 128 run on kernels sized for them; wider
+ * heads, up to 256 (the FlyDSL post, "FMHA through AOTriton", runs head
+ * dims up to 256 with two K/V blocks resident and gives 512 a body of its
+ * own), run on an 8-wave form of the prefill kernel for every Q, decode
+ * included; the fp32 path stops at 128.
  *
  * seqlens_k is never read on the host.  Values outside [0, K] are a caller
  * error; the kernels clamp them to [0, K] so memory outside the tensors is
@@ -66,7 +73,7 @@ enum attn_status {
  *   ATTN_ERR_INVALID_ARG  a negative size; Hq > 0 with Hkv == 0 or
  *                         Hq % Hkv != 0; a non-finite scale; q/o/lse NULL
  *                         while B*Hq*Q > 0; k/v NULL while B*Hkv*K > 0;
- *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 128]; or one
+ *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 256]; or one
  *                         (batch, head) slice of 2 GiB or more in bf16
  *                         (Q*D, Q*Dv, K*D or K*Dv >= 2^30 elements);
  *   ATTN_ERR_OOM, ATTN_ERR_HIP as above;

@@ -43,7 +43,8 @@ BAD = [
     (1, 4, 2, 8, 8, 64, 64, float("inf"), af.ATTN_ERR_INVALID_ARG),
     (1, 4, 2, 8, 8, 72, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),     # D % 16
     (1, 4, 2, 8, 8, 64, 7, 1.0, af.ATTN_ERR_UNSUPPORTED),
-    (1, 4, 2, 8, 8, 256, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 128
+    (1, 4, 2, 8, 8, 272, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 256
+    (1, 4, 2, 8, 8, 64, 512, 1.0, af.ATTN_ERR_UNSUPPORTED),
     (1, 4, 2, 8, 8, 0, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),
     (1, 4, 2, 8, 1 << 23, 128, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*D = 2^30: a 2 GiB slice
     (1, 4, 2, 8, 1 << 23, 64, 128, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*Dv = 2^30
@@ -57,6 +58,17 @@ def test_bad_arguments_rejected_before_launch(fn, case):
     B, Hq, Hkv, Q, K, D, Dv, scale, want = case
     fake = 1 << 20  # never dereferenced: the checks come first
     assert fn(fake, fake, fake, fake, fake, B, Hq, Hkv, Q, K, D, Dv, None, 0, scale, None) == want
+
+
+def test_wide_heads_only_on_the_16bit_path():
+    fake = 1 << 20
+    for D, Dv in [(256, 256), (144, 64), (64, 256)]:
+        st = af.attn_fwd_f32(fake, fake, fake, fake, fake, 1, 4, 2, 8, 8, D, Dv, None, 0, 1.0, None)
+        assert st == af.ATTN_ERR_UNSUPPORTED, (D, Dv)
+        assert af.attn_fwd_plan(1, 4, 2, 8, 8, D, Dv)["path"] == af.PATH_PREFILL
+    # Every Q of a wide head takes the prefill kernel (no decode kernel that wide).
+    assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 256, 256)["path"] == af.PATH_PREFILL
+    assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 128, 128)["path"] == af.PATH_DECODE
 
 
 @pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
@@ -177,10 +189,17 @@ def test_plan_prefill_splits(monkeypatch):
     assert af.attn_fwd_plan(1, 4, 2, 65, 0, 64, 64)["split_workers"] == 1
     # At most 32 pieces; the override is clamped the same way.
     assert af.attn_fwd_plan(1, 1, 1, 128, 1 << 20, 64, 64)["split_workers"] == 32
+    # Lean tiles (decode with wide heads: 8 packed rows) over long keys:
+    # pieces of 32 blocks whatever the tile count.
+    assert af.attn_fwd_plan(64, 64, 8, 1, 32768, 256, 256)["split_workers"] == 16
+    assert af.attn_fwd_plan(64, 64, 8, 1, 2047, 256, 256)["split_workers"] == 1
+    # Pieces hold a fixed number of blocks: a count is rounded to what whole
+    # pieces of ceil(blocks / count) blocks need.
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "7")
-    p = af.attn_fwd_plan(1, 4, 2, 65, 100, 64, 96)
+    p = af.attn_fwd_plan(1, 4, 2, 65, 1000, 64, 96)   # 16 blocks: pieces of 3, 6 of them
     # 130 packed rows per group: 2 tiles, 2 groups.
-    assert p["split_workers"] == 7 and p["partial_slots"] == 4 * 7 and p["workspace_bytes"] == 28 * 128 * 98 * 4
+    assert p["split_workers"] == 6 and p["partial_slots"] == 4 * 6 and p["workspace_bytes"] == 24 * 128 * 98 * 4
+    assert af.attn_fwd_plan(1, 4, 2, 65, 100, 64, 96)["split_workers"] == 2   # 2 blocks
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "1000")
-    assert af.attn_fwd_plan(1, 4, 2, 65, 100, 64, 64)["split_workers"] == 32
+    assert af.attn_fwd_plan(1, 4, 2, 65, 100000, 64, 64)["split_workers"] == 32
     # The fp32 path is never split (it has no plan of its own: D, Dv checks only).

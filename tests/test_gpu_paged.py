@@ -76,6 +76,8 @@ CASES = [
     (2, 16, 2, 60, 1024, 128, 128, 128, 0, "bf16", True, [1024, 317]),   # packed tiles across heads
     (3, 8, 2, 33, 512, 64, 64, 64, 31, "f16", True, [512, 0, 200]),
     (2, 32, 4, 100, 768, 128, 128, 256, 0, "bf16", False, [768, 129]),
+    (2, 8, 2, 150, 1024, 256, 256, 128, 0, "bf16", True, [1024, 500]),    # wide heads
+    (3, 8, 2, 1, 2048, 256, 256, 64, 0, "f16", True, [2048, 0, 999]),
 ]
 
 

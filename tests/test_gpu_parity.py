@@ -113,11 +113,18 @@ SPLIT_SHAPES = [
 ]
 
 
+def _pieces(K, splits):
+    """Pieces of ceil(blocks / splits) 64-key blocks that cover K keys."""
+    blocks = -(-K // 64)
+    per = -(-blocks // splits)
+    return -(-blocks // per)
+
+
 @pytest.mark.parametrize("splits", [2, 3, 7, 32])
 @pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_prefill_forced_splits(orc, shape, splits, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", str(splits))
-    assert af.attn_fwd_plan(*shape)["split_workers"] == splits
+    assert af.attn_fwd_plan(*shape)["split_workers"] == _pieces(shape[4], splits)
     B = shape[0]
     sl = np.array([shape[4], 0, shape[4] // 3][:B], np.int32)
     dtype = "f16" if splits == 3 else "bf16"
@@ -126,6 +133,44 @@ def test_prefill_forced_splits(orc, shape, splits, monkeypatch):
     _check(w, window=100, orc=orc, tag=f" splits={splits} W=100")
     w = inputs.Workload("split_nc", *shape, dtype=dtype, seqlens=sl, causal=False)
     _check(w, orc=orc, tag=f" splits={splits}")
+
+
+# Heads wider than 128 (up to 256): the 8-wave prefill form, for every Q
+# (decode shapes included: packed rows and split key ranges), padded widths
+# (D or Dv below 256), D != Dv, causal and not, windows, empty sequences.
+WIDE = [
+    (1, 4, 2, 64, 128, 256, 256),
+    (2, 8, 2, 300, 700, 256, 256),
+    (1, 8, 2, 1, 2053, 256, 256),     # decode: 8 packed rows, split keys
+    (2, 16, 8, 3, 999, 256, 256),
+    (2, 16, 8, 200, 333, 192, 256),
+    (1, 4, 4, 130, 90, 256, 128),     # more rows than keys, Dv padded
+    (1, 4, 2, 65, 131, 144, 80),
+    (1, 8, 1, 100, 4100, 256, 256),   # MQA, long keys: split
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "x".join(map(str, s)))
+def test_wide_heads(orc, shape, dtype, causal):
+    assert af.attn_fwd_plan(*shape)["path"] == af.PATH_PREFILL
+    w = inputs.Workload("wide", *shape, dtype=dtype, causal=causal)
+    _check(w, orc=orc)
+    B = shape[0]
+    sl = np.array([shape[4], 0, 7][:B], np.int32) if B > 1 else None
+    if sl is not None:
+        _check(inputs.Workload("wide_varlen", *shape, dtype=dtype, causal=causal, seqlens=sl), orc=orc)
+    if causal:
+        _check(w, window=70, orc=orc, tag=" W=70")
+
+
+@pytest.mark.parametrize("splits", [3, 32])
+def test_wide_heads_forced_splits(orc, splits, monkeypatch):
+    monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", str(splits))
+    w = inputs.Workload("wide_split", 2, 8, 2, 100, 1000, 256, 192, seqlens=np.array([1000, 77], np.int32))
+    _check(w, orc=orc, tag=f" splits={splits}")
+    _check(w, window=300, orc=orc, tag=f" splits={splits} W=300")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
