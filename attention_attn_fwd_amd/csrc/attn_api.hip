@@ -99,6 +99,8 @@ int prefill_splits(int B, int Hkv, int Q, int group, int K) {
     const int v = std::atoi(e);
     if (v >= 1) return std::min(v, kPrefillMaxSplits);
   }
+  // The combine pass runs one wave per output row, four to a workgroup.
+  if ((int64_t)B * Hkv * group * Q > INT32_MAX) return 1;
   const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
   constexpr int64_t kSlots = 512, kCUs = 256;
   const int64_t blocks = ((int64_t)K + kPrefillBN - 1) / kPrefillBN;

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   }
 }
 
-// Combine pass of split-KV prefill: one wave per tile row merges the row's
+// Combine pass of split-KV prefill: one wave per output row merges the row's
 // n_split partial states in split order (the merge of two online-softmax
 // states: rescale both to the larger max, add sums and accumulators), then
 // normalises and writes O and the LSE.  Lane l owns channels CPL*l ..
@@ -601,17 +601,26 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
   using E = Elem<F16>;
   constexpr int U = 8;
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // Output row (b, h, q), then the tile that holds it (the inverse of
+  // prefill_tile_of): its rank rem in the group and the row within it.
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)p.B * p.Hq * p.Q) return;
+  const int q = (int)(row % p.Q);
+  const int bh = (int)(row / p.Q);
+  const int b = bh / p.Hq, h = bh - b * p.Hq;
+  const int kh = h / p.group, hg = h - kh * p.group;
+  const int grp = b * p.Hkv + kh;
   const int per_grp = prefill_group_tiles(p.Q, p.group);
-  const int r_local = (int)(wid % kPrefillBM);
-  const int64_t tg = wid / kPrefillBM;
-  const int rem = (int)(tg % per_grp), grp = (int)(tg / per_grp);
-  if (grp >= p.B * p.Hkv) return;
-  const PrefillTile tile = prefill_tile_of(p, grp, rem);
-  const int r = tile.r0 + r_local;
-  if (r >= tile.n_rows) return;
-  const int hh = r / p.Q, q = r - hh * p.Q;
-  const int64_t row = ((int64_t)tile.b * p.Hq + tile.h_base + hh) * p.Q + q;
+  int rem, r_local;
+  if (prefill_packed(p.Q, p.group)) {
+    const int r = hg * p.Q + q;  // row of the group's list
+    rem = per_grp - 1 - r / kPrefillBM;
+    r_local = r % kPrefillBM;
+  } else {
+    const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
+    rem = (n_qt - 1 - q / kPrefillBM) * p.group + hg;
+    r_local = q % kPrefillBM;
+  }
   // Slot of piece s: ((grp * n_split + s) * per_grp + rem) * 128 + r_local.
   const int64_t slot0 = ((int64_t)grp * p.n_split * per_grp + rem) * kPrefillBM + r_local;
   const int64_t slot_step = (int64_t)per_grp * kPrefillBM;
@@ -689,7 +698,7 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
   hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * NW), args, 0, stream);
   if (e != hipSuccess || p.n_split <= 1) return e;
-  const dim3 cgrid((unsigned)(tiles * kPrefillBM / 4));
+  const dim3 cgrid((unsigned)(((int64_t)p.B * p.Hq * p.Q + 3) / 4));  // one wave per output row
   constexpr int CPL = DVP <= 128 ? 2 : 4;
   const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, CPL>)
                           : reinterpret_cast<const void*>(&prefill_combine_kernel<false, CPL>);
