@@ -55,9 +55,9 @@ int launch_status(hipError_t e) {
   return ATTN_ERR_HIP;
 }
 
-// Head widths: multiples of 16 up to 256 on the 16-bit MFMA kernels (above
-// 128 the 8-wave prefill form), up to 128 on the fp32 kernel.
-bool supported_width(int d, bool mfma) { return d >= 16 && d <= (mfma ? 256 : 128) && d % 16 == 0; }
+// Head widths: multiples of 16 up to 512 on the 16-bit MFMA kernels (above
+// 128 the 8-wave prefill forms), up to 128 on the fp32 kernel.
+bool supported_width(int d, bool mfma) { return d >= 16 && d <= (mfma ? 512 : 128) && d % 16 == 0; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -150,18 +150,20 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   } else {
     plan->path = 1;
     const int bm = bf16 ? kPrefillBM : kF32Rows;
-    // Workgroup indices are int; a split pass launches fewer than 512 tiles
-    // times at most kPrefillMaxSplits pieces.
+    // Workgroup indices are int: tiles x pieces x output-channel parts.
     if ((int64_t)((Q + bm - 1) / bm) * Hq * B > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
     if (bf16) {
+      const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
+      const int dv_parts = (D > 256 || Dv > 256) ? (Dv + 255) / 256 : 1;
+      if (tiles * dv_parts > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
       // Pieces of a fixed number of blocks: the requested count rounded to
       // what whole pieces of ceil(blocks / count) blocks need.
       const int want = prefill_splits(B, Hkv, Q, group, K);
       const int blocks = (K + kPrefillBN - 1) / kPrefillBN;
-      const int ns = want > 1 ? (blocks + prefill_split_blocks(K, want) - 1) / prefill_split_blocks(K, want) : 1;
+      int ns = want > 1 ? (blocks + prefill_split_blocks(K, want) - 1) / prefill_split_blocks(K, want) : 1;
+      if (tiles * ns * dv_parts > (int64_t)INT32_MAX) ns = 1;
       plan->split_workers = ns;
       if (ns > 1) {
-        const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
         plan->partial_slots = (int)(tiles * ns);
         plan->workspace_bytes = (int64_t)plan->partial_slots * kPrefillBM * (Dv + 2) * 4;
       }
@@ -219,6 +221,7 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   }
 
   p.n_split = 1;
+  p.dv_parts = (D > 256 || Dv > 256) ? (Dv + 255) / 256 : 1;
   if (!bf16) return launch_status(launch_fwd_f32(p, stream));
   if (plan.path == 1 && plan.split_workers <= 1) return launch_status(launch_prefill_bf16(p, stream));
 
@@ -297,7 +300,7 @@ const char* attn_fwd_strerror(int status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED:
-      return "unsupported size (D and Dv must be multiples of 16 in [16, 256], [16, 128] in fp32)";
+      return "unsupported size (D and Dv must be multiples of 16 in [16, 512], [16, 128] in fp32)";
     case ATTN_ERR_OOM: return "scratch allocation failed";
     case ATTN_ERR_HIP: return "HIP launch or runtime error";
     default: return "unknown status";

@@ -84,6 +84,7 @@ struct Params {
   int rows;                // group * Q
   int n_split;             // prefill: key-range pieces per tile (1: no split)
   int split_blocks;        // prefill: 64-key blocks per piece (piece s starts s * split_blocks into the tile's range)
+  int dv_parts;            // prefill, heads over 256: output-channel parts of 256 (1 otherwise)
   // Paged K/V cache (block_table null: contiguous k [B,Hkv,K,D], v [B,Hkv,K,Dv]).
   // Otherwise k [num_pages,Hkv,2^page_shift,D], v [num_pages,Hkv,2^page_shift,Dv]
   // and keys [j << page_shift, (j + 1) << page_shift) of sequence b are in page
@@ -104,7 +105,7 @@ hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
 constexpr int kMinPageShift = 6;
 
 // Padded widths the kernels are instantiated for.
-inline int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+inline int pad_width(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : (d <= 256 ? 256 : 512)); }
 
 // Row q of sequence b sits at absolute position q + row_delta: K_b - Q
 // (bottom-right alignment), or, without the causal limit, far enough past

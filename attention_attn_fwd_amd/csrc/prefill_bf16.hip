@@ -54,8 +54,10 @@ namespace attn {
 // LDS ring: K of stage 0, K of stage 1, V of stage 0, V of stage 1, so every
 // read offset that depends on the stage or the key tile fits the 16-bit
 // immediate of a ds_read.
-template <int DP, int DVP, int NW>
+template <int DP, int DVP, int NW, int BN_ = kPrefillBN>
 struct PrefillShape {
+  static constexpr int BN = BN_;            // keys per block
+  static constexpr int KT = BN / 16;        // 16-key MFMA tiles per block
   static constexpr int NT = kPrefillBM / (16 * NW);  // 16-row MFMA tiles per wave
   static constexpr int KS = DP / 32;        // 32-deep k-steps of Q.K
   static constexpr int JV = DVP / 16;       // 16-wide dv tiles of O^T
@@ -63,8 +65,8 @@ struct PrefillShape {
   static constexpr int VCH = DVP / 8;
   static constexpr int KROWB = DP * 2;      // LDS bytes per K row
   static constexpr int VROWB = DVP * 2;
-  static constexpr int K_TILE = kPrefillBN * KROWB;
-  static constexpr int V_TILE = kPrefillBN * VROWB;
+  static constexpr int K_TILE = BN * KROWB;
+  static constexpr int V_TILE = BN * VROWB;
   static constexpr int V_BASE = 2 * K_TILE;
   static constexpr int LDS = 2 * (K_TILE + V_TILE);
   static constexpr int ROUND = NW * 1024;   // bytes one wave-wide 16-byte load round of the workgroup covers
@@ -73,11 +75,17 @@ struct PrefillShape {
   static constexpr int K_ROWS_PER_LOAD = ROUND / KROWB;  // tile rows one load round covers
   static constexpr int V_ROWS_PER_LOAD = ROUND / VROWB;
   static_assert(NT * 16 * NW == kPrefillBM && (NT == 1 || NT == 2), "tile geometry");
+  static_assert((BN == 32 || BN == 64) && kPrefillBN % BN == 0, "block size");
   static_assert(K_TILE % ROUND == 0 && V_TILE % ROUND == 0, "load split");
-  // A load round covers whole swizzle periods, so a lane's chunk is the same
-  // in every round (periods: 16 rows or fewer for K, VCH / 2 for V).
-  static_assert(K_ROWS_PER_LOAD % (KCH < 16 ? KCH : 16) == 0 && V_ROWS_PER_LOAD % (VCH / 2) == 0, "swizzle");
-  static_assert(K_TILE + 3 * 16 * KROWB < 65536 && V_TILE + 48 * VROWB < 65536, "ds_read immediates");
+  // Swizzle periods in rows: 16 or fewer for K, VCH / 2 for V.  A load round
+  // covers whole periods (a lane fetches the same chunk in every round), or
+  // a period spans K_VAR rounds that cycle through K_VAR lane offsets.
+  static constexpr int K_PERIOD = KCH < 16 ? KCH : 16;
+  static constexpr int K_VAR = K_ROWS_PER_LOAD % K_PERIOD == 0 ? 1 : K_PERIOD / K_ROWS_PER_LOAD;
+  static_assert(K_VAR == 1 || (K_PERIOD % K_ROWS_PER_LOAD == 0 && K_LOADS % K_VAR == 0), "K swizzle");
+  static_assert(V_ROWS_PER_LOAD % (VCH / 2) == 0, "V swizzle");
+  static_assert(K_TILE + (KT - 1) * 16 * KROWB < 65536 && V_TILE + (32 * (KT / 2 - 1) + 16) * VROWB < 65536,
+                "ds_read immediates");
   static_assert(LDS <= 160 * 1024, "LDS of a CU");
 };
 
@@ -86,7 +94,7 @@ struct PrefillShape {
 // piece `split` of its key range.  `part` numbers (group, split, tile)
 // triples; it indexes the partial states of a split pass.
 struct PrefillTile {
-  int b, kh, h_base, r0, n_rows, split, part;
+  int b, kh, h_base, r0, n_rows, split, part, dv_part;
 };
 
 // Tile `rem` of group `grp` (rank order: heaviest causal tile first, heads
@@ -108,29 +116,33 @@ __device__ __forceinline__ PrefillTile prefill_tile_of(const Params& p, int grp,
   }
   t.split = 0;
   t.part = 0;
+  t.dv_part = 0;
   return t;
 }
 
 // Block index -> tile.  A virtual group is a (piece, group) pair.  When the
 // virtual groups divide evenly over the 8 XCDs (workgroup i runs on XCD
 // i % 8), each XCD gets whole virtual groups and finishes one (all its
-// tiles, heaviest first) before the next, so the workgroups resident on an
-// XCD stream the same K/V through its L2; otherwise the order is heaviest
-// tile first with virtual groups fastest.
+// tiles, heaviest first, and both output-channel parts of a tile next to
+// each other) before the next, so the workgroups resident on an XCD stream
+// the same K/V through its L2; otherwise the order is heaviest tile first
+// with virtual groups fastest.
 __device__ __forceinline__ PrefillTile prefill_tile(const Params& p) {
   const int x = blockIdx.x;
   const int vgroups = p.B * p.Hkv * p.n_split;
   const int per_grp = prefill_group_tiles(p.Q, p.group);
-  int vg, rem;
+  const int per_vg = per_grp * p.dv_parts;  // workgroups per virtual group
+  int vg, remx;
   if ((vgroups & 7) == 0) {
     const int xcd = x & 7, slot = x >> 3;
-    const int gi = slot / per_grp;
-    rem = slot - gi * per_grp;
+    const int gi = slot / per_vg;
+    remx = slot - gi * per_vg;
     vg = gi * 8 + xcd;
   } else {
-    rem = x / vgroups;
-    vg = x - rem * vgroups;
+    remx = x / vgroups;
+    vg = x - remx * vgroups;
   }
+  const int rem = remx / p.dv_parts, dv_part = remx - rem * p.dv_parts;
   // Split-major: virtual group vg is piece vg / groups of group vg % groups,
   // so an XCD gets every piece of its groups (pieces late in a range are
   // often empty; dealing pieces to XCDs would leave the XCDs that got the
@@ -139,6 +151,7 @@ __device__ __forceinline__ PrefillTile prefill_tile(const Params& p) {
   const int split = vg / groups, grp = vg - split * groups;
   PrefillTile t = prefill_tile_of(p, grp, rem);
   t.split = split;
+  t.dv_part = dv_part;
   t.part = (grp * p.n_split + split) * per_grp + rem;  // a row's pieces lie 128 rows apart
   return t;
 }
@@ -160,15 +173,18 @@ __device__ __forceinline__ void row_q_range(int r0, int r1, int Q, int* qlo, int
 // no channel is padding (the common case); otherwise padded channels read zero.
 // F16: the 16-bit inputs and output are IEEE binary16 instead of bf16.
 // PAGED: K and V live in a paged cache (Params::block_table).
-template <int DP, int DVP, int NW, bool EXACT, bool F16, bool PAGED>
+template <int DP, int DVP, int NW, int BN_, bool DVSPLIT, bool EXACT, bool F16, bool PAGED>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p) {
-  using S = PrefillShape<DP, DVP, NW>;
-  constexpr int NT = S::NT;
+  using S = PrefillShape<DP, DVP, NW, BN_>;
+  constexpr int NT = S::NT, KT = S::KT;
   constexpr int ROWS_W = 16 * NT;  // rows per wave
   using E = Elem<F16>;
-  constexpr int BN = kPrefillBN;
+  constexpr int BN = S::BN;
   const int D = EXACT ? DP : p.D;
-  const int Dv = EXACT ? DVP : p.Dv;
+  // DVSPLIT: this workgroup computes channels [dv0, dv0 + DVP) of the Dv_all
+  // output channels (part dv0 / DVP of p.dv_parts); the scores are the same
+  // for every part.  Dv is the width of this part.
+  const int Dv_all = DVSPLIT ? p.Dv : (EXACT ? DVP : p.Dv);
   __shared__ __attribute__((aligned(16))) unsigned char ring[S::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -177,6 +193,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
 
   const PrefillTile tile = prefill_tile(p);
   const int b = tile.b, kh = tile.kh, Q = p.Q;
+  const int dv0 = DVSPLIT ? tile.dv_part * DVP : 0;
+  const int Dv = DVSPLIT ? min(DVP, Dv_all - dv0) : Dv_all;
+  const bool lead = !DVSPLIT || tile.dv_part == 0;  // writes the row statistics (m, l, LSE)
 
   const int Kb = clamp_len(p.seqlens, b, p.K);
   const int delta = row_delta(Kb, Q, p.causal_shift);  // absolute position of query row q is q + delta
@@ -190,10 +209,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   const int kv_lo = W > 0 ? max(0, tq_lo + delta - W + 1) : 0;
   int jb0 = kv_lo / BN;
   int jb1 = kv_hi > kv_lo ? (kv_hi + BN - 1) / BN : jb0;
-  if (p.n_split > 1) {  // this workgroup's piece: split_blocks blocks, or what is left of them
-    const int64_t s0 = (int64_t)jb0 + (int64_t)tile.split * p.split_blocks;
+  if (p.n_split > 1) {  // this workgroup's piece: split_blocks 64-key blocks, or what is left of them
+    const int64_t pb = (int64_t)p.split_blocks * (kPrefillBN / BN);
+    const int64_t s0 = (int64_t)jb0 + (int64_t)tile.split * pb;
     jb0 = (int)min((int64_t)jb1, s0);
-    jb1 = (int)min((int64_t)jb1, s0 + p.split_blocks);
+    jb1 = (int)min((int64_t)jb1, s0 + pb);
   }
 
   // Wave-level (scalar) row range and the positions its rows span.
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // An empty piece of a split pass (past the end of this tile's range): its
   // rows saw no key here.  The condition is uniform over the workgroup.
   if (p.n_split > 1 && jb0 >= jb1) {
-    if (wave_has_rows && g4 == 0) {
+    if (lead && wave_has_rows && g4 == 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (row_ok[t]) {
@@ -263,17 +283,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // fetches the global chunk the swizzle puts there.  A round covers a whole
   // number of swizzle periods of rows, so the chunk a lane fetches is the same
   // in every round and its global offset advances by a fixed step.
-  auto lane_off = [&](int rowb, bool is_v, int width) -> uint32_t {
+  // Round r of a tile covers rows r * ROWS_PER_LOAD onward; `first_row`
+  // shifts the lane's row for the K_VAR offsets of a K swizzle period.
+  auto lane_off = [&](int rowb, bool is_v, int stride, int col0, int width, int first_row) -> uint32_t {
     const int off = wave * 1024 + 16 * lane;
-    const int row = off / rowb, pos = (off % rowb) >> 4;
+    const int row = off / rowb + first_row, pos = (off % rowb) >> 4;
     const int ch = pos ^ (is_v ? swz_v<S::VCH>(row) : swz_k<S::KCH>(row));
-    if (EXACT) return (uint32_t)(row * width + ch * 8) * 2;
-    return ch < width / 8 ? (uint32_t)(row * width + ch * 8) * 2 : kOutOfRange;
+    if (EXACT) return (uint32_t)(row * stride + col0 + ch * 8) * 2;
+    return ch < width / 8 ? (uint32_t)(row * stride + col0 + ch * 8) * 2 : kOutOfRange;
   };
-  const uint32_t koff = lane_off(S::KROWB, false, D);
-  const uint32_t voff = lane_off(S::VROWB, true, Dv);
-  const uint32_t kstep = (uint32_t)(S::K_ROWS_PER_LOAD * D * 2);
-  const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv * 2);
+  uint32_t koff[S::K_VAR];
+#pragma unroll
+  for (int v = 0; v < S::K_VAR; ++v) koff[v] = lane_off(S::KROWB, false, D, 0, D, v * S::K_ROWS_PER_LOAD);
+  const uint32_t voff = lane_off(S::VROWB, true, Dv_all, dv0, Dv, 0);
+  const uint32_t kstep = (uint32_t)(S::K_VAR * S::K_ROWS_PER_LOAD * D * 2);
+  const uint32_t vstep = (uint32_t)(S::V_ROWS_PER_LOAD * Dv_all * 2);
   const uint32_t lds0 = lds_offset(ring);
   // Block jb's loads; `page` holds its keys when the cache is paged (blocks
   // never straddle a page), read from the table a block ahead of its use.
@@ -282,24 +306,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     const KvSpan sp = kv_span_t<PAGED>(p, b, kh, kb0, page);
     const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
     const rsrc_t rk = slice_rsrc(sp.k, rows_left * D * 2);
-    const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv * 2);
+    const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv_all * 2);
     const uint32_t kbase = lds0 + stg * S::K_TILE + wave * 1024;
     const uint32_t vbase = lds0 + S::V_BASE + stg * S::V_TILE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(rk, kbase + i * S::ROUND, koff + i * kstep);
+    for (int i = 0; i < S::K_LOADS; ++i)
+      load_lds16(rk, kbase + i * S::ROUND, koff[i % S::K_VAR] + (i / S::K_VAR) * kstep);
 #pragma unroll
     for (int i = 0; i < S::V_LOADS; ++i) load_lds16(rv, vbase + i * S::ROUND, voff + i * vstep);
   };
 
   // Per-lane LDS read offsets (stage 0).  K fragment of k-step s, key tile i:
   // row 16i + l16, chunk (4s + g4) ^ swz_k(row); swz_k(row) = swz_k(l16) for
-  // every i.  V^T fragment of dv tile j: rows 32kk + 4*g4 + l16/4 (+16), chunk
+  // every i, below 16, so k-step s reads at ka[s % 4] + 256 * (s / 4).  V^T
+  // fragment of dv tile j: rows 32kk + 4*g4 + l16/4 (+16), chunk
   // (2j + (l16 & 3)/2) ^ swz_v(row), half (l16 & 1); swz_v is the same for
   // every kk and for the +16 row.
-  uint32_t ka[S::KS], va[S::JV];
+  constexpr int KA = S::KS < 4 ? S::KS : 4;
+  uint32_t ka[KA], va[S::JV];
 #pragma unroll
-  for (int s = 0; s < S::KS; ++s)
+  for (int s = 0; s < KA; ++s)
     ka[s] = lds0 + l16 * S::KROWB + ((((4 * s + g4) ^ swz_k<S::KCH>(l16))) << 4);
+  auto k_addr = [&](int st) { return ka[st % 4] + 256 * (st / 4); };
   {
     const int vrow = 4 * g4 + (l16 >> 2);
 #pragma unroll
@@ -335,7 +363,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // r) is legal for query position pq iff lo <= x <= hi, with hi from
   // causality and K_b and lo from the window: one unsigned compare against an
   // immediate x per element.
-  auto mask_bias = [&](int kb0, f32x4 (&s)[4][NT]) {
+  auto mask_bias = [&](int kb0, f32x4 (&s)[KT][NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int rel = q_row[t] + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
@@ -344,7 +372,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
       const uint32_t span = (uint32_t)(hi - lo);
       const bool none = hi < lo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < KT; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool legal = !none & ((uint32_t)(16 * i + r - lo) <= span);
@@ -358,15 +386,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // factor c is positive, so -inf * c stays -inf).
   // Column max over the block in log2 units (-inf: no legal key; c > 0 keeps
   // -inf * c at -inf): per-lane v_max3 chain, then the four lane groups.
-  auto block_max = [&](const f32x4 (&s)[4][NT], int t) {
+  auto block_max = [&](const f32x4 (&s)[KT][NT], int t) {
     float mx = max3f(s[0][t][0], s[0][t][1], s[0][t][2]);
     mx = max3f(mx, s[0][t][3], s[1][t][0]);
     mx = max3f(mx, s[1][t][1], s[1][t][2]);
-    mx = max3f(mx, s[1][t][3], s[2][t][0]);
-    mx = max3f(mx, s[2][t][1], s[2][t][2]);
-    mx = max3f(mx, s[2][t][3], s[3][t][0]);
-    mx = max3f(mx, s[3][t][1], s[3][t][2]);
-    mx = max2f(mx, s[3][t][3]);
+    if constexpr (KT == 4) {
+      mx = max3f(mx, s[1][t][3], s[2][t][0]);
+      mx = max3f(mx, s[2][t][1], s[2][t][2]);
+      mx = max3f(mx, s[2][t][3], s[3][t][0]);
+      mx = max3f(mx, s[3][t][1], s[3][t][2]);
+      mx = max2f(mx, s[3][t][3]);
+    } else {
+      static_assert(KT == 2, "block of 32 or 64 keys");
+      mx = max2f(mx, s[1][t][3]);
+    }
     return group4_max(mx) * c;
   };
 
@@ -377,14 +410,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // stays; no block max is computed.  Otherwise, or while a row has no
   // reference yet, the column max moves the reference, the accumulators are
   // rescaled and the weights recomputed (rare: a few blocks per row).
-  auto softmax = [&](const f32x4 (&s)[4][NT], bf16x8 (&pf)[NT][2]) {
-    f32x4 e[4][NT];
+  auto softmax = [&](const f32x4 (&s)[KT][NT], bf16x8 (&pf)[NT][KT / 2]) {
+    f32x4 e[KT][NT];
     float rs[NT];
     auto weights = [&](int t) {
       const float mneg = m_run[t] == -INFINITY ? 0.f : -m_run[t];
       float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < KT; ++i) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           e[i][t][r] = fast_exp2(fmaf(s[i][t][r], c, mneg));
@@ -415,8 +448,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       l_run[t] += rs[t];
-      pf[t][0] = E::pack(e[0][t], e[1][t]);
-      pf[t][1] = E::pack(e[2][t], e[3][t]);
+#pragma unroll
+      for (int kk = 0; kk < KT / 2; ++kk) pf[t][kk] = E::pack(e[2 * kk][t], e[2 * kk + 1][t]);
     }
   };
 
@@ -430,24 +463,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     constexpr uint32_t KOFF = STG * S::K_TILE, VOFF = STG * S::V_TILE;
     {
       const int kb0 = jb * BN;
-      f32x4 s[4][NT];
+      f32x4 s[KT][NT];
       // S^T = K Q^T.  The K fragments of k-step st + 1 are read while the
       // MFMAs of k-step st run; the fences keep the compiler from hoisting
       // every read of the block (64 registers) ahead of the products.
       auto qk = [&](auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
-        bf16x8 ak[2][4];
+        bf16x8 ak[2][KT];
         if constexpr (!FULL) mask_bias(kb0, s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ak[0][i] = lds_read_b128(ka[0] + KOFF + 16 * i * S::KROWB);
+        for (int i = 0; i < KT; ++i) ak[0][i] = lds_read_b128(k_addr(0) + KOFF + 16 * i * S::KROWB);
 #pragma unroll
         for (int st = 0; st < S::KS; ++st) {
           if (st + 1 < S::KS) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ak[(st + 1) & 1][i] = lds_read_b128(ka[st + 1] + KOFF + 16 * i * S::KROWB);
+            for (int i = 0; i < KT; ++i)
+              ak[(st + 1) & 1][i] = lds_read_b128(k_addr(st + 1) + KOFF + 16 * i * S::KROWB);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < KT; ++i) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               const f32x4 c0 = (FULL && st == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : s[i][t];
@@ -469,14 +503,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
       av[0][0] = read_v(0, 0);
       av[0][1] = read_v(0, 1);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 pf[NT][2];
+      bf16x8 pf[NT][KT / 2];
       softmax(s, pf);
       __builtin_amdgcn_sched_barrier(0);
-      // O^T += V^T P^T over two 32-key halves, two dv tiles per step with the
-      // next step's fragments in flight.  The contraction index e of the B
-      // operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 + e - 4,
-      // the S^T register layout; the V^T fragment is read in the same order.
-      constexpr int NP = 2 * (S::JV / 2);  // steps of two dv tiles over both halves
+      // O^T += V^T P^T over the block's 32-key halves, two dv tiles per step
+      // with the next step's fragments in flight.  The contraction index e of
+      // the B operand maps to key 32kk + 4*g4 + e (e < 4) or 32kk + 16 + 4*g4 +
+      // e - 4, the S^T register layout; the V^T fragment is read in the same
+      // order.
+      constexpr int NP = (KT / 2) * (S::JV / 2);  // steps of two dv tiles over the halves
 #pragma unroll
       for (int n = 0; n < NP; ++n) {
         const int kk = n / (S::JV / 2), j = 2 * (n % (S::JV / 2));
@@ -547,12 +582,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
       const float lt = group4_sum(l_run[t]);
       if (row_ok[t]) {
         const int64_t slot = part_slot(t);
-        if (g4 == 0) {
+        if (lead && g4 == 0) {
           p.ws_m[slot] = lt > 0.f ? m_run[t] : -INFINITY;
           p.ws_l[slot] = lt;
         }
         if (lt > 0.f) {
-          float* arow = p.ws_acc + slot * Dv;
+          float* arow = p.ws_acc + slot * Dv_all + dv0;
 #pragma unroll
           for (int j = 0; j < S::JV; ++j) {
             const int dv = 16 * j + 4 * g4;
@@ -569,7 +604,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (row_ok[t]) {
       const int64_t row = row_index(t);
-      uint16_t* orow = static_cast<uint16_t*>(p.o) + row * Dv;
+      uint16_t* orow = static_cast<uint16_t*>(p.o) + row * Dv_all + dv0;
 #pragma unroll
       for (int j = 0; j < S::JV; ++j) {
         const int dv = 16 * j + 4 * g4;
@@ -582,7 +617,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
           *reinterpret_cast<ushort4*>(orow + dv) = ov;
         }
       }
-      if (g4 == 0) p.lse[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+      if (lead && g4 == 0) p.lse[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 }
@@ -591,13 +626,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
 // n_split partial states in split order (the merge of two online-softmax
 // states: rescale both to the larger max, add sums and accumulators), then
 // normalises and writes O and the LSE.  Lane l owns channels CPL*l ..
-// CPL*l + CPL - 1 (CPL = 2 up to 128 channels, 4 up to 256).
+// CPL*l + CPL - 1 (CPL = 2 up to 128 channels, 4 up to 256, 8 up to 512).
 // The pieces are taken eight at a time, all their loads issued together, and
 // folded into a running (M, L, o); a piece with m = -inf has no acc (never
 // written) and is skipped.
+struct alignas(32) float8_t {
+  float4 lo, hi;
+};
 template <bool F16, int CPL>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
-  using V = std::conditional_t<CPL == 2, float2, float4>;
+  using V = std::conditional_t<CPL == 2, float2, std::conditional_t<CPL == 4, float4, float8_t>>;
+  static_assert(sizeof(V) == CPL * sizeof(float), "channels per lane");
   using E = Elem<F16>;
   constexpr int U = 8;
   const int lane = threadIdx.x & 63;
@@ -667,52 +706,60 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
       ov.y = E::cvt(o[1] * inv);
       *reinterpret_cast<ushort2*>(orow) = ov;
     } else {
-      ushort4 ov;
-      ov.x = E::cvt(o[0] * inv);
-      ov.y = E::cvt(o[1] * inv);
-      ov.z = E::cvt(o[2] * inv);
-      ov.w = E::cvt(o[3] * inv);
-      *reinterpret_cast<ushort4*>(orow) = ov;
+#pragma unroll
+      for (int c4 = 0; c4 < CPL; c4 += 4) {
+        ushort4 ov;
+        ov.x = E::cvt(o[c4] * inv);
+        ov.y = E::cvt(o[c4 + 1] * inv);
+        ov.z = E::cvt(o[c4 + 2] * inv);
+        ov.w = E::cvt(o[c4 + 3] * inv);
+        *reinterpret_cast<ushort4*>(orow + c4) = ov;
+      }
     }
   }
   if (lane == 0) p.lse[row] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
-template <int DP, int DVP, int NW>
+template <int DP, int DVP, int NW, int BN, bool DVSPLIT>
 static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const int64_t tiles = (int64_t)prefill_group_tiles(p.Q, p.group) * p.Hkv * p.B;
-  const dim3 grid((unsigned)(tiles * p.n_split));
+  const dim3 grid((unsigned)(tiles * p.n_split * p.dv_parts));
   Params arg = p;
   void* args[] = {&arg};
   const void* const kernels[8] = {
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, false, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, false, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, true, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, true, false>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, false, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, false, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, false, true, true>),
-      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, true, true, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, false, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, true, false, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, false, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, true, true, false>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, false, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, true, false, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, false, true, true>),
+      reinterpret_cast<const void*>(&prefill_bf16_kernel<DP, DVP, NW, BN, DVSPLIT, true, true, true>),
   };
-  const int exact = p.D == DP && p.Dv == DVP;
+  const int exact = p.D == DP && p.Dv == DVP * p.dv_parts;
   const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
   hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * NW), args, 0, stream);
   if (e != hipSuccess || p.n_split <= 1) return e;
   const dim3 cgrid((unsigned)(((int64_t)p.B * p.Hq * p.Q + 3) / 4));  // one wave per output row
-  constexpr int CPL = DVP <= 128 ? 2 : 4;
+  constexpr int CPL = DVP * (DVSPLIT ? 2 : 1) <= 128 ? 2 : (DVP * (DVSPLIT ? 2 : 1) <= 256 ? 4 : 8);
   const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, CPL>)
                           : reinterpret_cast<const void*>(&prefill_combine_kernel<false, CPL>);
   return hipLaunchKernel(cfn, cgrid, dim3(256), args, 0, stream);
 }
 
-// Heads wider than 128 (padded to 256 on both sides) take the 8-wave form.
+// Heads up to 128 wide: 4 waves of 32 rows, 64-key blocks.  Up to 256 (padded
+// to 256 on both sides): 8 waves of 16 rows.  Up to 512: 8 waves of 16 rows
+// over 32-key blocks of 512 channels, and the output channels in parts of 256
+// computed by separate workgroups that each recompute the scores (the
+// accumulators of 512 channels would not fit a wave's registers).
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream) {
   const int dp = pad_width(p.D), dvp = pad_width(p.Dv);
-  if (dp > 128 || dvp > 128) return launch_prefill_t<256, 256, 8>(p, stream);
-  if (dp == 64 && dvp == 64) return launch_prefill_t<64, 64, 4>(p, stream);
-  if (dp == 64 && dvp == 128) return launch_prefill_t<64, 128, 4>(p, stream);
-  if (dp == 128 && dvp == 64) return launch_prefill_t<128, 64, 4>(p, stream);
-  return launch_prefill_t<128, 128, 4>(p, stream);
+  if (dp > 256 || dvp > 256) return launch_prefill_t<512, 256, 8, 32, true>(p, stream);
+  if (dp > 128 || dvp > 128) return launch_prefill_t<256, 256, 8, 64, false>(p, stream);
+  if (dp == 64 && dvp == 64) return launch_prefill_t<64, 64, 4, 64, false>(p, stream);
+  if (dp == 64 && dvp == 128) return launch_prefill_t<64, 128, 4, 64, false>(p, stream);
+  if (dp == 128 && dvp == 64) return launch_prefill_t<128, 64, 4, 64, false>(p, stream);
+  return launch_prefill_t<128, 128, 4, 64, false>(p, stream);
 }
 
 }  // namespace attn

@@ -164,8 +164,8 @@ def run_options(args, torch, af, inputs):
     timed alone: fp16 storage (causal prefill, decode), the non-causal mode
     (bf16 prefill, every key legal for every row), a paged K/V cache (pages of
     256 keys for the prefill, 128 for the decode, in random order), and two
-    chunked-prefill shapes (short query runs against a long cache), and heads
-    of 256 channels on the step's two shapes."""
+    chunked-prefill shapes (short query runs against a long cache), heads of
+    256 channels on the step's two shapes and of 512 on the prefill shape."""
     import dataclasses
     c3, c5 = inputs.config(3), inputs.config(5)
     cases = [
@@ -182,7 +182,8 @@ def run_options(args, torch, af, inputs):
               ("prefill_chunk512", inputs.Workload("chunk512_ctx32k_b1_prefill", 1, 32, 8, 512, 32768, 128, 128))]
     # Heads of 256 (the 8-wave kernel form), on the step's two shapes.
     cases += [("prefill_d256", dataclasses.replace(c3, name="c3_shape_d256_prefill", D=256, Dv=256)),
-              ("decode_d256", dataclasses.replace(c5, name="c5_shape_d256_decode", D=256, Dv=256))]
+              ("decode_d256", dataclasses.replace(c5, name="c5_shape_d256_decode", D=256, Dv=256)),
+              ("prefill_d512", dataclasses.replace(c3, name="c3_shape_d512_prefill", D=512, Dv=512))]
     hbm_bound = {"prefill_chunk64"}
     pages = {"prefill_paged": 256, "decode_paged": 128}
     stream = torch.cuda.current_stream()
@@ -211,7 +212,7 @@ def run_options(args, torch, af, inputs):
         del pr
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "options: fp16 storage, non-causal mode, paged K/V cache, chunked prefill, "
-                                "head dim 256, % of roofline",
+                                "head dim 256 and 512, % of roofline",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic: seeded N(0,1) rounded to the storage type (Philox-4x32-10, seed 1234)",
                       "calls": parts, "kernel_digest": kernel_digest()}), flush=True)

@@ -37,10 +37,12 @@
  * streams do not share scratch.
  *
  * Head widths: D and Dv up to 128 run on kernels sized for them; wider
- * heads, up to 256 (the FlyDSL post, "FMHA through AOTriton", runs head
- * dims up to 256 with two K/V blocks resident and gives 512 a body of its
- * own), run on an 8-wave form of the prefill kernel for every Q, decode
- * included; the fp32 path stops at 128.
+ * heads run on 8-wave forms of the prefill kernel for every Q, decode
+ * included: up to 256 with two 64-key K/V blocks resident, up to 512 with
+ * 32-key blocks and the output channels in parts of 256 on separate
+ * workgroups that each recompute the scores (the FlyDSL post, "FMHA through
+ * AOTriton", gives 512 a body of its own for the same LDS reason: two
+ * resident 512-wide blocks do not fit).  The fp32 path stops at 128.
  *
  * seqlens_k is never read on the host.  Values outside [0, K] are a caller
  * error; the kernels clamp them to [0, K] so memory outside the tensors is
@@ -73,7 +75,8 @@ enum attn_status {
  *   ATTN_ERR_INVALID_ARG  a negative size; Hq > 0 with Hkv == 0 or
  *                         Hq % Hkv != 0; a non-finite scale; q/o/lse NULL
  *                         while B*Hq*Q > 0; k/v NULL while B*Hkv*K > 0;
- *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 256]; or one
+ *   ATTN_ERR_UNSUPPORTED  D or Dv not a multiple of 16 in [16, 512]
+ *                         ([16, 128] for the fp32 path); or one
  *                         (batch, head) slice of 2 GiB or more in bf16
  *                         (Q*D, Q*Dv, K*D or K*Dv >= 2^30 elements);
  *   ATTN_ERR_OOM, ATTN_ERR_HIP as above;

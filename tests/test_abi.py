@@ -43,8 +43,9 @@ BAD = [
     (1, 4, 2, 8, 8, 64, 64, float("inf"), af.ATTN_ERR_INVALID_ARG),
     (1, 4, 2, 8, 8, 72, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),     # D % 16
     (1, 4, 2, 8, 8, 64, 7, 1.0, af.ATTN_ERR_UNSUPPORTED),
-    (1, 4, 2, 8, 8, 272, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 256
-    (1, 4, 2, 8, 8, 64, 512, 1.0, af.ATTN_ERR_UNSUPPORTED),
+    (1, 4, 2, 8, 8, 528, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # beyond 512
+    (1, 4, 2, 8, 8, 64, 528, 1.0, af.ATTN_ERR_UNSUPPORTED),
+    (1, 4, 2, 8, 8, 504, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),    # not a multiple of 16
     (1, 4, 2, 8, 8, 0, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),
     (1, 4, 2, 8, 1 << 23, 128, 64, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*D = 2^30: a 2 GiB slice
     (1, 4, 2, 8, 1 << 23, 64, 128, 1.0, af.ATTN_ERR_UNSUPPORTED),  # K*Dv = 2^30
@@ -62,7 +63,7 @@ def test_bad_arguments_rejected_before_launch(fn, case):
 
 def test_wide_heads_only_on_the_16bit_path():
     fake = 1 << 20
-    for D, Dv in [(256, 256), (144, 64), (64, 256)]:
+    for D, Dv in [(256, 256), (144, 64), (64, 256), (512, 512), (512, 64), (400, 272)]:
         st = af.attn_fwd_f32(fake, fake, fake, fake, fake, 1, 4, 2, 8, 8, D, Dv, None, 0, 1.0, None)
         assert st == af.ATTN_ERR_UNSUPPORTED, (D, Dv)
         assert af.attn_fwd_plan(1, 4, 2, 8, 8, D, Dv)["path"] == af.PATH_PREFILL

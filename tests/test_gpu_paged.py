@@ -78,6 +78,8 @@ CASES = [
     (2, 32, 4, 100, 768, 128, 128, 256, 0, "bf16", False, [768, 129]),
     (2, 8, 2, 150, 1024, 256, 256, 128, 0, "bf16", True, [1024, 500]),    # wide heads
     (3, 8, 2, 1, 2048, 256, 256, 64, 0, "f16", True, [2048, 0, 999]),
+    (2, 8, 2, 90, 512, 512, 512, 64, 0, "bf16", True, [512, 200]),        # 512 wide: 32-key blocks
+    (2, 4, 2, 1, 1024, 384, 448, 128, 0, "f16", False, [1024, 3]),
 ]
 
 

@@ -165,12 +165,40 @@ def test_wide_heads(orc, shape, dtype, causal):
         _check(w, window=70, orc=orc, tag=" W=70")
 
 
+# Heads wider than 256 (up to 512): 32-key blocks of 512 channels, output
+# channels in parts of 256 on separate workgroups (each recomputes the
+# scores); D and Dv padded, one part or two, decode through packed rows.
+WIDE512 = [
+    (1, 4, 2, 64, 128, 512, 512),
+    (2, 8, 2, 200, 300, 512, 512),
+    (1, 8, 2, 1, 1000, 512, 512),
+    (2, 4, 4, 70, 333, 384, 448),     # padded D, a second part of 192 channels
+    (1, 4, 2, 65, 131, 512, 128),     # one part
+    (1, 8, 1, 100, 2100, 320, 512),   # MQA, long keys: split
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE512, ids=lambda s: "x".join(map(str, s)))
+def test_wide_heads_512(orc, shape, dtype, causal):
+    assert af.attn_fwd_plan(*shape)["path"] == af.PATH_PREFILL
+    w = inputs.Workload("wide512", *shape, dtype=dtype, causal=causal)
+    _check(w, orc=orc)
+    if shape[0] > 1:
+        sl = np.array([shape[4], 0][:shape[0]], np.int32)
+        _check(inputs.Workload("wide512_varlen", *shape, dtype=dtype, causal=causal, seqlens=sl), orc=orc)
+    if causal:
+        _check(w, window=50, orc=orc, tag=" W=50")
+
+
 @pytest.mark.parametrize("splits", [3, 32])
 def test_wide_heads_forced_splits(orc, splits, monkeypatch):
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", str(splits))
-    w = inputs.Workload("wide_split", 2, 8, 2, 100, 1000, 256, 192, seqlens=np.array([1000, 77], np.int32))
-    _check(w, orc=orc, tag=f" splits={splits}")
-    _check(w, window=300, orc=orc, tag=f" splits={splits} W=300")
+    for D, Dv in [(256, 192), (512, 400)]:
+        w = inputs.Workload("wide_split", 2, 8, 2, 100, 1000, D, Dv, seqlens=np.array([1000, 77], np.int32))
+        _check(w, orc=orc, tag=f" splits={splits}")
+        _check(w, window=300, orc=orc, tag=f" splits={splits} W=300")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
