@@ -35,6 +35,17 @@
  * (ldq, ldk, ldv, ldo) are in elements, so tests can embed V and O in wider
  * rows and check that columns beyond Dv are never read or written.
  *
+ * The backward (oracle_attn_bwd) gives the gradients of the scalar
+ * sum(dO * O) with respect to q, k and v (no cotangent on the LSE output):
+ * per row, the weights P over the legal keys as above; dV[k] += P[k] dO;
+ * dP[k] = dO . V[k]; the softmax Jacobian applied to dP, dS[k] = P[k] (dP[k]
+ * - sum_j P[j] dP[j]); dQ = scale sum_k dS[k] K[k]; dK[k] += scale dS[k] q.
+ * A kv-head's dK and dV sum the contributions of all its query heads.  These
+ * are the chain rule through scores, softmax and the weighted sum, written in
+ * those steps; the FlyDSL post ("FMHA through AOTriton") describes the
+ * separate dQ and dK/dV passes of the GPU backward, which compute the same
+ * quantities.  Input dtype 3 (double) exists for finite-difference checks.
+ *
  * ORACLE_MUTANT (compile-time, tests only) plants one known mistake so the
  * pin tests can show they would catch it; the default build defines none.
  */
@@ -75,6 +86,7 @@ static double load_elem(const void* base, int dtype, int64_t i) {
     return (double)f;
   }
   if (dtype == 2) return half_to_double(((const uint16_t*)base)[i]);
+  if (dtype == 3) return ((const double*)base)[i];
   return (double)((const float*)base)[i];
 }
 
@@ -193,7 +205,7 @@ static void oracle_row(const void* q, const void* k, const void* v, int dtype, i
 static int check_args(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens, int window,
                       int causal, int dtype) {
   if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return -1;
-  if (dtype < 0 || dtype > 2) return -1;
+  if (dtype < 0 || dtype > 3) return -1;
   if (!causal && window > 0) return -1;
   if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return -1;
   if (seqlens)
@@ -312,4 +324,116 @@ int64_t oracle_attn_probs(const void* q, const void* k, int dtype, int B, int Hq
   free(scores);
   free(lg);
   return n_legal;
+}
+
+/*
+ * Backward of one (batch, kv-head) group: every row of its query heads.
+ * Adds into dk, dv of the group (zeroed by the caller) and writes dq rows.
+ */
+static void oracle_bwd_group(const void* q, const void* k, const void* v, const void* dout, int dtype, double* dq,
+                             double* dk, double* dv, int Hq, int Hkv, int Q, int K, int D, int Dv,
+                             const int32_t* seqlens, int window, int causal, double scale, int b, int kh,
+                             double* scores, unsigned char* is_legal, double* pw, double* dp) {
+  const int g = Hq / Hkv;
+  const int64_t kbase = ((int64_t)b * Hkv + kh) * (int64_t)K;
+  for (int hh = 0; hh < g; ++hh) {
+    const int h = kh * g + hh;
+    for (int qi = 0; qi < Q; ++qi) {
+      const int64_t r = ((int64_t)b * Hq + h) * Q + qi;
+      for (int d = 0; d < D; ++d) dq[r * D + d] = 0.0;
+      int64_t n_legal = row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, causal, scale, D, D, b, h, qi,
+                                   scores, is_legal);
+      if (n_legal == 0) continue;
+      /* The row's weights, as in the forward. */
+      double m = -INFINITY;
+      for (int64_t kk = 0; kk < K; ++kk)
+        if (is_legal[kk] && scores[kk] > m) m = scores[kk];
+      double l = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk)
+        if (is_legal[kk]) l += exp(scores[kk] - m);
+      for (int64_t kk = 0; kk < K; ++kk) {
+#if ORACLE_MUTANT == 18 /* dV from unnormalised weights */
+        pw[kk] = is_legal[kk] ? exp(scores[kk] - m) : 0.0;
+#else
+        pw[kk] = is_legal[kk] ? exp(scores[kk] - m) / l : 0.0;
+#endif
+      }
+      /* dV[k] += P[k] dO; dP[k] = dO . V[k]. */
+      double delta = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk) {
+        if (!is_legal[kk]) continue;
+        double acc = 0.0;
+        for (int j = 0; j < Dv; ++j) {
+          const double g_o = load_elem(dout, dtype, r * Dv + j);
+#if ORACLE_MUTANT == 19 /* dV accumulated into the wrong kv-head's rows */
+          const int64_t vrow = (((int64_t)b * Hkv + (h % Hkv)) * (int64_t)K + kk) * Dv;
+#else
+          const int64_t vrow = (kbase + kk) * Dv;
+#endif
+          dv[vrow + j] += pw[kk] * g_o;
+          acc += g_o * load_elem(v, dtype, (kbase + kk) * Dv + j);
+        }
+        dp[kk] = acc;
+        delta += pw[kk] * acc;
+      }
+      /* dS[k] = P[k] (dP[k] - delta); dQ += scale dS[k] K[k]; dK[k] += scale dS[k] q. */
+      const int64_t qrow = r * D;
+      for (int64_t kk = 0; kk < K; ++kk) {
+        if (!is_legal[kk]) continue;
+#if ORACLE_MUTANT == 16 /* the softmax Jacobian's delta term dropped */
+        const double ds = pw[kk] * dp[kk];
+#else
+        const double ds = pw[kk] * (dp[kk] - delta);
+#endif
+        for (int d = 0; d < D; ++d) {
+          dq[qrow + d] += scale * ds * load_elem(k, dtype, (kbase + kk) * D + d);
+#if ORACLE_MUTANT == 17 /* scale missing from dK */
+          dk[(kbase + kk) * D + d] += ds * load_elem(q, dtype, qrow + d);
+#else
+          dk[(kbase + kk) * D + d] += scale * ds * load_elem(q, dtype, qrow + d);
+#endif
+        }
+      }
+    }
+  }
+}
+
+/*
+ * Full backward: dq [B,Hq,Q,D], dk [B,Hkv,K,D], dv [B,Hkv,K,Dv] (dense rows),
+ * dout [B,Hq,Q,Dv] in the input dtype.  Keys past K_b get zero gradients.
+ * Returns 0, or a negative code as oracle_attn_fwd does.
+ */
+int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype, double* dq, double* dk,
+                    double* dv, int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens,
+                    int window, double scale, int threads, int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, dtype);
+  if (rc) return rc;
+  const int64_t groups = (int64_t)B * Hkv;
+  memset(dk, 0, sizeof(double) * (size_t)(groups * K * D));
+  memset(dv, 0, sizeof(double) * (size_t)(groups * K * Dv));
+  if (Hq == 0 || Q == 0) return 0;
+  int bad = 0;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+  {
+    const size_t n = (size_t)(K > 0 ? K : 1);
+    double* scores = (double*)malloc(sizeof(double) * n);
+    unsigned char* lg = (unsigned char*)malloc(n);
+    double* pw = (double*)malloc(sizeof(double) * n);
+    double* dp = (double*)malloc(sizeof(double) * n);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t gi = 0; gi < groups; ++gi) {
+      if (!scores || !lg || !pw || !dp) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      oracle_bwd_group(q, k, v, dout, dtype, dq, dk, dv, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, scale,
+                       (int)(gi / Hkv), (int)(gi % Hkv), scores, lg, pw, dp);
+    }
+    free(scores);
+    free(lg);
+    free(pw);
+    free(dp);
+  }
+  return bad ? -3 : 0;
 }

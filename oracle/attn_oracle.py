@@ -6,7 +6,9 @@ legal keys k <= q + K_b - Q (K_b replaces K for per-sequence lengths), an
 optional window of W keys ending at the diagonal, O = 0 / LSE = -inf for rows
 without a legal key; with causal=False every key k < K_b is legal for every
 row (no window).  Inputs are host arrays: bf16 as uint16 bit patterns,
-float32, or IEEE binary16 (numpy float16).  Results are float64.
+float32, IEEE binary16 (numpy float16) or float64 (for finite-difference
+checks).  Results are float64.  `bwd` gives the gradients of sum(dO * O)
+with respect to q, k and v.
 """
 from __future__ import annotations
 
@@ -30,6 +32,8 @@ def _setup(lib):
     lib.oracle_attn_fwd_rows.restype = ci
     lib.oracle_attn_probs.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci, ci, ci, vp, ci]
     lib.oracle_attn_probs.restype = i64
+    lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci, ci]
+    lib.oracle_attn_bwd.restype = ci
     return lib
 
 
@@ -49,7 +53,9 @@ def _dtype_code(arr: np.ndarray) -> int:
         return 1
     if arr.dtype == np.float16:
         return 2
-    raise TypeError("oracle inputs are bf16 bit patterns (uint16), float32 or float16")
+    if arr.dtype == np.float64:
+        return 3
+    raise TypeError("oracle inputs are bf16 bit patterns (uint16), float32, float16 or float64")
 
 
 def _threads(threads: int) -> int:
@@ -154,3 +160,29 @@ class Oracle:
         if n < 0:
             raise OracleError(f"oracle_attn_probs returned {n}")
         return p[:K], int(n)
+
+    def bwd(self, q, k, v, dout, *, seqlens=None, window=0, scale=None, threads=0, causal=True):
+        """Gradients of sum(dout * O) w.r.t. q, k, v (dense [B,H,T,width] inputs, dout
+        [B,Hq,Q,Dv] in the same dtype).  Returns (dq, dk, dv) float64."""
+        B, Hq, Q, D = q.shape
+        _, Hkv, K, _ = k.shape
+        Dv = v.shape[-1]
+        code = _dtype_code(q)
+        for a in (k, v, dout):
+            assert _dtype_code(a) == code
+        for a in (q, k, v, dout):
+            assert a.flags.c_contiguous
+        assert dout.shape == (B, Hq, Q, Dv)
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        dq = np.empty((B, Hq, Q, D), dtype=np.float64)
+        dk = np.empty((B, Hkv, K, D), dtype=np.float64)
+        dv = np.empty((B, Hkv, K, Dv), dtype=np.float64)
+        sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
+        rc = self.lib.oracle_attn_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, code,
+                                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, B, Hq, Hkv, Q, K, D, Dv,
+                                      None if sl is None else sl.ctypes.data, int(window), float(scale),
+                                      _threads(threads), int(bool(causal)))
+        if rc:
+            raise OracleError(f"oracle_attn_bwd returned {rc}")
+        return dq, dk, dv

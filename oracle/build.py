@@ -29,7 +29,13 @@ MUTANTS = {
     13: "LSE in base 2",
     14: "causal limit kept for non-causal rows",
     15: "fp16 exponent bias off by one",
+    16: "backward: softmax Jacobian delta term dropped",
+    17: "backward: scale missing from dK",
+    18: "backward: dV from unnormalised weights",
+    19: "backward: dV accumulated into kv-head h % Hkv",
 }
+# Mutants of the backward only; the forward pins cannot see them.
+BWD_MUTANTS = (16, 17, 18, 19)
 
 
 def _compile(out, defines=()):

@@ -430,10 +430,145 @@ def pin_brute_force(orc):
         _close(lse, bl, 1e-12, f"brute force LSE {B,Hq,Hkv,Q,K,D,Dv,sl,st,causal}")
 
 
+# ---------------------------------------------------------------------------
+# Backward (gradients of sum(dO * O) w.r.t. q, k, v)
+# ---------------------------------------------------------------------------
+
+def _loss(orc, q, k, v, dout, **kw):
+    o, _ = orc.fwd(q, k, v, **kw)
+    return float(np.sum(dout * o))
+
+
+def pin_bwd_finite_differences(orc):
+    """Every gradient element against a central difference of the (pinned)
+    fp64 forward: sum(dO * O(x + e)) - sum(dO * O(x - e)) over 2e, float64 inputs."""
+    rng = np.random.default_rng(40)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 4, 2, 3, 6, 4, 3
+    cases = [dict(seqlens=np.array([6, 2], np.int32)), dict(window=2), dict(causal=False, seqlens=np.array([4, 6], np.int32)),
+             dict(scale=-0.7)]
+    for kw in cases:
+        q = rng.standard_normal((B, Hq, Q, D))
+        k = rng.standard_normal((B, Hkv, K, D))
+        v = rng.standard_normal((B, Hkv, K, Dv))
+        dout = rng.standard_normal((B, Hq, Q, Dv))
+        dq, dk, dv = orc.bwd(q, k, v, dout, **kw)
+        eps = 1e-5
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for i in np.ndindex(x.shape):
+                x0 = x[i]
+                x[i] = x0 + eps
+                lp = _loss(orc, q, k, v, dout, **kw)
+                x[i] = x0 - eps
+                lm = _loss(orc, q, k, v, dout, **kw)
+                x[i] = x0
+                num[i] = (lp - lm) / (2 * eps)
+            _close(g, num, 1e-7, f"d{name} vs central differences {sorted(kw)}")
+
+
+def _torch_attention(q, k, v, kb, window, causal, scale):
+    """Plain masked attention in torch float64 (kv heads repeated over groups)."""
+    B, Hq, Q, D = q.shape
+    Hkv, K = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    ke = k.repeat_interleave(g, dim=1)
+    ve = v.repeat_interleave(g, dim=1)
+    s = scale * torch.matmul(q, ke.transpose(-1, -2))
+    kpos = torch.arange(K).view(1, K)
+    outs = []
+    for b in range(B):
+        p = torch.arange(Q).view(Q, 1) + int(kb[b]) - Q
+        m = kpos < int(kb[b])
+        if causal:
+            m = m & (kpos <= p)
+        if window > 0:
+            m = m & (kpos > p - window)
+        sb = s[b].masked_fill(~m, float("-inf"))
+        w = torch.softmax(sb, dim=-1)
+        w = torch.nan_to_num(w, nan=0.0)  # rows with no legal key
+        outs.append(torch.matmul(w, ve[b]))
+    return torch.stack(outs)
+
+
+def pin_bwd_torch_autograd(orc):
+    """Gradients against torch autograd through plain masked attention in float64."""
+    rng = np.random.default_rng(41)
+    for (B, Hq, Hkv, Q, K, D, Dv), kw in [((2, 4, 2, 7, 9, 8, 6), dict(seqlens=[9, 3])),
+                                           ((1, 6, 3, 5, 5, 16, 16), dict(window=3)),
+                                           ((2, 4, 1, 4, 11, 8, 12), dict(causal=False, seqlens=[0, 11])),
+                                           ((1, 2, 2, 12, 6, 4, 4), dict())]:
+        q = rng.standard_normal((B, Hq, Q, D))
+        k = rng.standard_normal((B, Hkv, K, D))
+        v = rng.standard_normal((B, Hkv, K, Dv))
+        dout = rng.standard_normal((B, Hq, Q, Dv))
+        sl = kw.get("seqlens")
+        scale = 1.0 / math.sqrt(D)
+        okw = dict(window=kw.get("window", 0), causal=kw.get("causal", True))
+        if sl is not None:
+            okw["seqlens"] = np.array(sl, np.int32)
+        dq, dk, dv = orc.bwd(q, k, v, dout, **okw)
+        tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+        kb = sl if sl is not None else [K] * B
+        o = _torch_attention(tq, tk, tv, kb, okw["window"], okw["causal"], scale)
+        gq, gk, gv = torch.autograd.grad((o * torch.from_numpy(dout)).sum(), (tq, tk, tv))
+        what = f"{(B, Hq, Hkv, Q, K, D, Dv)} {kw}"
+        _close(dq, gq.numpy(), 1e-10, "dq vs torch autograd " + what)
+        _close(dk, gk.numpy(), 1e-10, "dk vs torch autograd " + what)
+        _close(dv, gv.numpy(), 1e-10, "dv vs torch autograd " + what)
+
+
+def pin_bwd_closed_forms(orc):
+    """(a) window 1: every row sees one key (weight 1): dQ = dK = 0 and dV[k] is
+    the sum of dO over the rows whose diagonal is k; (b) dO = 0: every gradient
+    is 0; (c) identical keys: uniform weights, dQ = 0 and dV[k] = mean of dO."""
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, Q, K, D, Dv = 1, 4, 2, 5, 8, 8, 4
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    dout = _f32(rng, (B, Hq, Q, Dv))
+    dq, dk, dv = orc.bwd(q, k, v, dout, window=1)
+    _close(dq, np.zeros_like(dq), 1e-15, "window 1: dQ")
+    _close(dk, np.zeros_like(dk), 1e-15, "window 1: dK")
+    want = np.zeros_like(dv)
+    g = Hq // Hkv
+    for h in range(Hq):
+        for qi in range(Q):
+            want[0, h // g, qi + K - Q] += dout[0, h, qi]
+    _close(dv, want, 1e-12, "window 1: dV")
+    dq, dk, dv = orc.bwd(q, k, v, np.zeros_like(dout))
+    for name, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _close(a, np.zeros_like(a), 0.0, f"dO = 0: {name}")
+    kc = np.ascontiguousarray(np.repeat(k[:, :, :1], K, axis=2))
+    dq, dk, dv = orc.bwd(q, kc, v, dout, causal=False)
+    _close(dq, np.zeros_like(dq), 1e-12, "identical keys: dQ")
+    want = np.zeros_like(dv)
+    for h in range(Hq):
+        want[0, h // g] += dout[0, h].astype(np.float64).sum(axis=0) / K
+    _close(dv, want, 1e-12, "identical keys: dV")
+
+
+def pin_bwd_gqa_sum(orc):
+    """A kv-head's dK/dV is the sum over its query heads of the MHA gradients
+    with K/V repeated; dQ is the same."""
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 6, 2, 4, 9, 8, 8
+    q, k, v = _f32(rng, (B, Hq, Q, D)), _f32(rng, (B, Hkv, K, D)), _f32(rng, (B, Hkv, K, Dv))
+    dout = _f32(rng, (B, Hq, Q, Dv))
+    sl = np.array([9, 5], np.int32)
+    dq, dk, dv = orc.bwd(q, k, v, dout, seqlens=sl, window=4)
+    g = Hq // Hkv
+    ke, ve = np.ascontiguousarray(np.repeat(k, g, axis=1)), np.ascontiguousarray(np.repeat(v, g, axis=1))
+    dq2, dk2, dv2 = orc.bwd(q, ke, ve, dout, seqlens=sl, window=4)
+    _close(dq, dq2, 1e-12, "GQA dQ equals MHA dQ")
+    _close(dk, dk2.reshape(B, Hkv, g, K, D).sum(axis=2), 1e-12, "GQA dK = sum of MHA dK over the group")
+    _close(dv, dv2.reshape(B, Hkv, g, K, Dv).sum(axis=2), 1e-12, "GQA dV = sum of MHA dV over the group")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_closed_forms, pin_bwd_gqa_sum]
+
 INDEPENDENT_PINS = [
     pin_worked_examples, pin_textbook_causal, pin_bottom_right, pin_uniform_v, pin_single_key,
     pin_scale_zero, pin_empty_rows, pin_shift_invariance, pin_probs_sum_to_one, pin_split_merge,
     pin_gqa_expand, pin_varlen_unpadded, pin_v_columns_untouched, pin_fp16_decode, pin_noncausal_textbook,
     pin_noncausal_key_order, pin_noncausal_closed_forms, pin_noncausal_needs_no_window,
 ]
-ALL_PINS = INDEPENDENT_PINS + [pin_brute_force]
+ALL_PINS = INDEPENDENT_PINS + BWD_PINS + [pin_brute_force]
