@@ -21,7 +21,8 @@ PATH_NONE, PATH_PREFILL, PATH_DECODE = 0, 1, 2
 ATTN_FWD_FP16, ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL = 1, 2, 4
 
 # Every function the header declares; a CPU test checks the library exports all of them.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_paged", "attn_fwd_strerror", "attn_fwd_plan")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_paged", "attn_bwd", "attn_fwd_strerror",
+           "attn_fwd_plan")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +57,8 @@ def load():
         lib.attn_fwd_ex.restype = ci
         lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, ci, ci, ci, vp, ci, cf, ci, vp]
         lib.attn_fwd_paged.restype = ci
+        lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, cf, ci, vp]
+        lib.attn_bwd.restype = ci
         lib.attn_fwd_strerror.argtypes = [ci]
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Plan)]
@@ -111,6 +114,14 @@ def attn_fwd_paged(q, k_pages, v_pages, o, lse, B, Hq, Hkv, Q, D, Dv, block_tabl
     return load().attn_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, D, Dv,
                                  _ptr(block_table), int(pages_per_seq), int(page_size), int(num_pages),
                                  _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags,
+             stream) -> int:
+    """Raw C call of the backward; returns the status."""
+    return load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                           B, Hq, Hkv, Q, K, D, Dv, _ptr(seqlens_k), int(window), float(scale), int(flags),
+                           _stream(stream))
 
 
 def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:
@@ -208,3 +219,30 @@ def forward_paged(q, k_pages, v_pages, block_table, seqlens_k=None, window: int 
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_paged")
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, seqlens_k=None, window: int = 0, scale: Optional[float] = None,
+             stream=None, causal: bool = True):
+    """Gradients of sum(dout * o) w.r.t. q, k, v on torch tensors (o and lse as the
+    forward returned them).  bfloat16 or float16, D and Dv up to 128.
+    Returns (dq, dk, dv) in the input dtype."""
+    import torch
+
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q, k, v, o, dout must all be bfloat16 or all float16")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, Hq, Q, D = q.shape
+    _, Hkv, K, Dv = v.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    flags = (ATTN_FWD_FP16 if q.dtype == torch.float16 else 0) | (0 if causal else ATTN_FWD_NONCAUSAL)
+    st = attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags,
+                  torch.cuda.current_stream() if stream is None else stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

@@ -25,7 +25,7 @@ LIB = os.path.join(HERE, "libattn_fwd.so")
 INPUTS_LIB = os.path.join(HERE, "libattn_inputs.so")
 ARCH = os.environ.get("ATTN_FWD_ARCH", "gfx950")
 
-HIP_SOURCES = ["attn_api.hip", "prefill_bf16.hip", "decode_bf16.hip", "fwd_f32.hip"]
+HIP_SOURCES = ["attn_api.hip", "prefill_bf16.hip", "decode_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

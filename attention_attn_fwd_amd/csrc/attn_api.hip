@@ -295,6 +295,70 @@ int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void
                    &pg);
 }
 
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens_k,
+             int window, float scale, int flags, void* stream_) {
+  using namespace attn;
+  constexpr int kKnown = ATTN_FWD_FP16 | ATTN_FWD_FP32 | ATTN_FWD_NONCAUSAL;
+  if ((flags & ~kKnown) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((flags & ATTN_FWD_FP16) && (flags & ATTN_FWD_FP32)) return ATTN_ERR_INVALID_ARG;
+  const bool causal = !(flags & ATTN_FWD_NONCAUSAL);
+  if (!causal && window > 0) return ATTN_ERR_INVALID_ARG;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq > 0 && (Hkv == 0 || Hq % Hkv != 0)) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)B * Hq * Q, keys = (int64_t)B * Hkv * K;
+  if (rows == 0 && keys == 0) return ATTN_OK;
+  if (flags & ATTN_FWD_FP32) return ATTN_ERR_UNSUPPORTED;
+  auto width_ok = [](int d) { return d >= 16 && d <= 128 && d % 16 == 0; };
+  if (!width_ok(D) || !width_ok(Dv)) return ATTN_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)Q * D * 2 >= lim || (int64_t)Q * Dv * 2 >= lim || (int64_t)K * D * 2 >= lim ||
+      (int64_t)K * Dv * 2 >= lim)
+    return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)((Q + 127) / 128) * Hq * B > (int64_t)INT32_MAX || (int64_t)((K + 127) / 128) * Hkv * B > INT32_MAX ||
+      (rows + 3) / 4 > (int64_t)INT32_MAX)
+    return ATTN_ERR_UNSUPPORTED;
+  if (keys > 0 && (!k || !v || !dk || !dv)) return ATTN_ERR_INVALID_ARG;
+  if (rows > 0 && (!q || !o || !lse || !dout || !dq)) return ATTN_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (ptr && !aligned16(ptr)) return ATTN_ERR_INVALID_ARG;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+  BwdParams p = {};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.seqlens = seqlens_k;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Q = Q; p.K = K; p.D = D; p.Dv = Dv;
+  p.window = window > 0 ? window : 0;
+  p.causal_shift = causal ? 0 : kNonCausalShift;
+  p.f16 = (flags & ATTN_FWD_FP16) ? 1 : 0;
+  p.group = Hkv > 0 ? Hq / Hkv : 1;
+  p.q_sign = scale < 0.f ? 1 : 0;
+  p.scale_log2 = std::fmax(std::fabs(scale) * 1.4426950408889634f, 1e-30f);
+  p.scale = scale;
+  p.abs_scale = std::fabs(scale);
+
+  // Scratch: delta and lse2 per row.
+  const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
+  if (fail && fail[0] == '1') return ATTN_ERR_OOM;
+  void* ws = nullptr;
+  if (rows > 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+    hipMemPool_t pool = nullptr;
+    if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipMallocFromPoolAsync(&ws, (size_t)(rows * 2 * 4), pool, stream) != hipSuccess || !ws) return ATTN_ERR_OOM;
+  }
+  p.delta = static_cast<float*>(ws);
+  p.lse2 = p.delta ? p.delta + rows : nullptr;
+  const int launched = launch_status(launch_bwd_bf16(p, stream));
+  if (ws) {
+    const hipError_t ef = hipFreeAsync(ws, stream);
+    if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;
+  }
+  return launched;
+}
+
 const char* attn_fwd_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

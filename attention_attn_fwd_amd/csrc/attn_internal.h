@@ -95,6 +95,28 @@ struct Params {
   int num_pages;
 };
 
+// Backward pass (gradients of sum(dO * O) w.r.t. q, k, v).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;           // forward output
+  const void* dout;        // dO [B,Hq,Q,Dv]
+  const float* lse;        // forward LSE [B,Hq,Q]
+  float* delta;            // scratch [B,Hq,Q]: rowsum(dO * O)
+  float* lse2;             // scratch [B,Hq,Q]: LSE * log2(e), +inf for rows without a key
+  void* dq;                // [B,Hq,Q,D]
+  void* dk;                // [B,Hkv,K,D]
+  void* dv;                // [B,Hkv,K,Dv]
+  const int32_t* seqlens;
+  int B, Hq, Hkv, Q, K, D, Dv;
+  int window, causal_shift, f16, group, q_sign;
+  float scale_log2;        // |scale| * log2(e), kept positive as in the forward
+  float scale;             // signed scale: dQ = scale * dS K
+  float abs_scale;         // dK = |scale| * dS^T (sign-adjusted q)
+};
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
+
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream);
 hipError_t launch_decode_bf16(const Params& p, hipStream_t stream);
@@ -349,6 +371,17 @@ __device__ __forceinline__ void load_lds16(rsrc_t rs, uint32_t lds_wave_base, ui
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voffset), "s"(rs)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// The 4-byte form: lane l's 4 bytes land at lds_wave_base + 4*l.
+__device__ __forceinline__ void load_lds4(rsrc_t rs, uint32_t lds_wave_base, uint32_t voffset) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(lds_wave_base), "v"(voffset), "s"(rs)
                : "memory", "m0");

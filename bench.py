@@ -111,9 +111,29 @@ class Problem:
         self.page, self.num_pages = page, len(used)
         self.host = None
 
+    def make_backward(self, af, torch):
+        """Turn the call into the backward: O and LSE from one forward call, a
+        seeded dO, and gradient buffers.  Algorithmic work: the four products
+        dV, dP (over Dv), dQ, dK (over D) and the recomputed S (over D) per
+        legal pair, 2 * (3D + 2Dv) flop."""
+        from attention_attn_fwd_amd import inputs
+        w = self.w
+        self.call(af, torch.cuda.current_stream())
+        dout = inputs.normal(w.o_shape(), 7, w.seed, w.dtype)
+        self.dout = torch.from_numpy(dout).to("cuda:0")
+        if w.dtype == "bf16":
+            self.dout = self.dout.view(torch.bfloat16)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        self.flops = 2.0 * (3 * w.D + 2 * w.Dv) * self.pairs
+        self.backward = True
+
     def call(self, af, stream):
         w = self.w
-        if getattr(self, "page", None):
+        if getattr(self, "backward", False):
+            flags = (af.ATTN_FWD_FP16 if w.dtype == "f16" else 0) | (0 if w.causal else af.ATTN_FWD_NONCAUSAL)
+            st = af.attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.dout, self.dq, self.dk, self.dv, w.B, w.Hq,
+                             w.Hkv, w.Q, w.K, w.D, w.Dv, self.seq, w.window, w.scale, flags, stream)
+        elif getattr(self, "page", None):
             flags = (af.ATTN_FWD_FP16 if w.dtype == "f16" else 0) | (0 if w.causal else af.ATTN_FWD_NONCAUSAL)
             st = af.attn_fwd_paged(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Q, w.D, w.Dv,
                                    self.table, w.K // self.page, self.page, self.num_pages, self.seq, w.window,
@@ -165,7 +185,8 @@ def run_options(args, torch, af, inputs):
     (bf16 prefill, every key legal for every row), a paged K/V cache (pages of
     256 keys for the prefill, 128 for the decode, in random order), and two
     chunked-prefill shapes (short query runs against a long cache), heads of
-    256 channels on the step's two shapes and of 512 on the prefill shape."""
+    256 channels on the step's two shapes and of 512 on the prefill shape, and
+    the backward at the prefill shape."""
     import dataclasses
     c3, c5 = inputs.config(3), inputs.config(5)
     cases = [
@@ -184,6 +205,8 @@ def run_options(args, torch, af, inputs):
     cases += [("prefill_d256", dataclasses.replace(c3, name="c3_shape_d256_prefill", D=256, Dv=256)),
               ("decode_d256", dataclasses.replace(c5, name="c5_shape_d256_decode", D=256, Dv=256)),
               ("prefill_d512", dataclasses.replace(c3, name="c3_shape_d512_prefill", D=512, Dv=512))]
+    # The backward (attn_bwd) at the dense prefill shape.
+    cases += [("backward", dataclasses.replace(c3, name="c3_shape_bf16_backward"))]
     hbm_bound = {"prefill_chunk64"}
     pages = {"prefill_paged": 256, "decode_paged": 128}
     stream = torch.cuda.current_stream()
@@ -192,6 +215,8 @@ def run_options(args, torch, af, inputs):
         pr = Problem(w, torch)
         if tag in pages:
             pr.paginate(pages[tag], torch)
+        if tag == "backward":
+            pr.make_backward(af, torch)
         for _ in range(args.warmup):
             pr.call(af, stream)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -202,7 +227,7 @@ def run_options(args, torch, af, inputs):
         ev[args.steps].record(stream)
         torch.cuda.synchronize()
         t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])) * 1e-3
-        if tag.startswith("prefill") and tag not in hbm_bound:
+        if (tag.startswith("prefill") or tag == "backward") and tag not in hbm_bound:
             achieved, peak, unit, bound = pr.flops / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = pr.kv_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
@@ -212,7 +237,7 @@ def run_options(args, torch, af, inputs):
         del pr
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "options: fp16 storage, non-causal mode, paged K/V cache, chunked prefill, "
-                                "head dim 256 and 512, % of roofline",
+                                "head dim 256 and 512, backward, % of roofline",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                       "data": "synthetic: seeded N(0,1) rounded to the storage type (Philox-4x32-10, seed 1234)",
                       "calls": parts, "kernel_digest": kernel_digest()}), flush=True)

@@ -134,6 +134,30 @@ int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void
                    int Hkv, int Q, int D, int Dv, const int32_t* block_table, int pages_per_seq, int page_size,
                    int num_pages, const int32_t* seqlens_k, int window, float scale, int flags, void* stream);
 
+/*
+ * Backward of attn_fwd_ex: the gradients of sum(dO * O) with respect to q, k
+ * and v (no gradient flows into the LSE output), for the same attention
+ * (causal unless ATTN_FWD_NONCAUSAL, window, seqlens_k, scale).  The FlyDSL
+ * post, "FMHA through AOTriton", describes this pass as separate dQ and dK/dV
+ * kernels that reuse the forward's layouts; a kv-head's dK and dV sum over
+ * its Hq/Hkv query heads.
+ *
+ * Inputs: q, k, v as given to the forward; o [B,Hq,Q,Dv] and lse [B,Hq,Q]
+ * (float) as the forward returned them for those inputs; dout [B,Hq,Q,Dv].
+ * Outputs: dq [B,Hq,Q,D], dk [B,Hkv,K,D], dv [B,Hkv,K,Dv], all in the
+ * storage type (bf16, or IEEE binary16 with ATTN_FWD_FP16); every element is
+ * written, keys at or past K_b get 0.  Sums are fp32; the weights and dS are
+ * rounded to the storage type for the matrix products.  Deterministic (no
+ * atomics).  Scratch (two floats per query row) comes from the same
+ * stream-ordered pool as the forward's.
+ *
+ * Returns as attn_fwd_ex, and ATTN_ERR_UNSUPPORTED for ATTN_FWD_FP32 or D, Dv
+ * outside multiples of 16 in [16, 128].
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens_k,
+             int window, float scale, int flags, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_fwd_strerror(int status);
 

@@ -204,3 +204,29 @@ def test_plan_prefill_splits(monkeypatch):
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "1000")
     assert af.attn_fwd_plan(1, 4, 2, 65, 100000, 64, 64)["split_workers"] == 32
     # The fp32 path is never split (it has no plan of its own: D, Dv checks only).
+
+
+def test_bwd_argument_checks():
+    fake = 1 << 20
+
+    def bwd(B=1, Hq=4, Hkv=2, Q=8, K=8, D=64, Dv=64, window=0, scale=1.0, flags=0, q=fake, dk=fake):
+        return af.attn_bwd(q, fake, fake, fake, fake, fake, fake, dk, fake, B, Hq, Hkv, Q, K, D, Dv, None, window,
+                           scale, flags, None)
+    bad, uns = af.ATTN_ERR_INVALID_ARG, af.ATTN_ERR_UNSUPPORTED
+    assert bwd(Hkv=3) == bad
+    assert bwd(B=-1) == bad
+    assert bwd(scale=float("nan")) == bad
+    assert bwd(flags=8) == bad
+    assert bwd(flags=af.ATTN_FWD_FP16 | af.ATTN_FWD_FP32) == bad
+    assert bwd(flags=af.ATTN_FWD_NONCAUSAL, window=4) == bad
+    assert bwd(q=None) == bad
+    assert bwd(dk=None) == bad
+    assert bwd(q=fake + 2) == bad
+    assert bwd(flags=af.ATTN_FWD_FP32) == uns
+    assert bwd(D=256) == uns
+    assert bwd(Dv=144) == uns
+    assert bwd(D=72) == uns
+    assert bwd(K=1 << 23, D=128) == uns
+    assert bwd(B=0) == af.ATTN_OK
+    assert af.attn_bwd(None, None, None, None, None, None, None, None, None, 2, 4, 2, 0, 0, 64, 64, None, 0, 1.0, 0,
+                       None) == af.ATTN_OK
