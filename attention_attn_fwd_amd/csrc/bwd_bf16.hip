@@ -8,15 +8,16 @@
 // Per row, with the forward's LSE: P = exp(S - LSE), dP = dO V^T,
 // delta = rowsum(dO * O) (= sum_k P dP), dS = P (dP - delta); then
 // dV = P^T dO, dK = scale dS^T q, dQ = scale dS K.  A kv-head's dK and dV sum
-// over its query heads.  Three passes, no atomics (bitwise reproducible):
-//   * bwd_prep_kernel: delta and LSE * log2(e) per row (+inf for a row with
-//     no legal key, so its weights are 0);
+// over its query heads.  Two passes, no atomics (bitwise reproducible):
 //   * bwd_dq_kernel: one workgroup per 128 query rows of one head, 8 waves of
 //     16 rows, streaming 64-key K and V blocks through a two-stage LDS ring
 //     by direct loads.  Per block: S^T = K q^T and dP^T = V dO^T with q and dO
 //     in registers (the forward's layout: a lane holds 4 keys of one row),
 //     dS^T in registers, then dQ^T += K^T dS^T with K^T read transposed
-//     (ds_read_b64_tr_b16) in the key order of the dS^T registers;
+//     (ds_read_b64_tr_b16) in the key order of the dS^T registers.  It also
+//     forms each row's delta (from the O and dO rows it loads) and LSE in
+//     log2 units (+inf for a row with no legal key, so its weights are 0),
+//     and stores both for the second pass;
 //   * bwd_dkdv_kernel: one workgroup per 128 keys of one kv-head, 8 waves of
 //     16 keys, K and V in registers, streaming 64-row blocks of q and dO (and
 //     the rows' LSE and delta) of every query head of the group.  Per block:
@@ -65,35 +66,6 @@ struct BwdShape {
   static_assert(A_TILE + 48 * AROWB + 1024 < 65536 && B_TILE + 48 * BROWB + 1024 < 65536, "ds_read immediates");
   static_assert(LDS <= 80 * 1024, "LDS");
 };
-
-// delta = rowsum(dO * O) and LSE in log2 units, one wave per row; lane l owns
-// channels 2l, 2l + 1 of each 128-channel step.
-template <bool F16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)p.B * p.Hq * p.Q) return;
-  const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * p.Dv;
-  const uint16_t* g = static_cast<const uint16_t*>(p.dout) + row * p.Dv;
-  auto widen = [](uint16_t h) -> float {
-    if constexpr (F16) return (float)__builtin_bit_cast(_Float16, h);
-    else return __builtin_bit_cast(float, (uint32_t)h << 16);
-  };
-  float acc = 0.f;
-  for (int c = 2 * lane; c < p.Dv; c += 128) {
-    const uint32_t ov = *reinterpret_cast<const uint32_t*>(o + c);
-    const uint32_t gv = *reinterpret_cast<const uint32_t*>(g + c);
-    acc = fmaf(widen((uint16_t)(ov & 0xFFFFu)), widen((uint16_t)(gv & 0xFFFFu)), acc);
-    acc = fmaf(widen((uint16_t)(ov >> 16)), widen((uint16_t)(gv >> 16)), acc);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) {
-    p.delta[row] = acc;
-    const float l = p.lse[row];
-    p.lse2[row] = l == -INFINITY ? INFINITY : l * 1.44269504088896340736f;
-  }
-}
 
 // Direct loads of two row tiles (A: width DP, B: width DVP) of kBwdBlock rows
 // into a two-stage ring, and the per-lane LDS addresses of their 16-byte
@@ -181,8 +153,10 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(bf16x8 x, uint32_t sign) {
 // dQ: workgroup = 128 query rows of head h of sequence b; wave w owns rows
 // 16w .. 16w + 15 (lane column l16).
 // ---------------------------------------------------------------------------
+// Two workgroups per CU (4 waves per SIMD, at most 128 VGPRs): 8% faster than
+// one on the dense prefill shape's backward.
 template <int DP, int DVP, bool EXACT, bool F16>
-__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_dq_kernel(BwdParams p) {
   using S = BwdShape<DP, DVP>;
   using E = Elem<F16>;
   constexpr int BN = kBwdBlock;
@@ -224,24 +198,45 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
   // q (sign-adjusted) and dO fragments: B operands of S^T = K q^T and dP^T = V dO^T.
+  // The row's O chunks at the dO chunks' channels give delta = rowsum(dO * O).
   bf16x8 qf[S::KS], gf[S::KSV];
+  float dlt = 0.f;
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + rowi * D;
     const uint16_t* grow = static_cast<const uint16_t*>(p.dout) + rowi * Dv;
+    const uint16_t* orow = static_cast<const uint16_t*>(p.o) + rowi * Dv;
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
       const int col = 32 * s + 8 * g4;
       qf[s] = neg_bf16x8(__builtin_bit_cast(bf16x8, (row_ok && col < D) ? load_u4(qrow + col) : zero_u4()), qx);
     }
+    auto widen = [](uint32_t h) -> float {
+      if constexpr (F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+      else return __builtin_bit_cast(float, h << 16);
+    };
 #pragma unroll
     for (int s = 0; s < S::KSV; ++s) {
       const int col = 32 * s + 8 * g4;
-      gf[s] = __builtin_bit_cast(bf16x8, (row_ok && col < Dv) ? load_u4(grow + col) : zero_u4());
+      const bool in = row_ok && col < Dv;
+      const uint4 gu = in ? load_u4(grow + col) : zero_u4();
+      const uint4 ou = in ? load_u4(orow + col) : zero_u4();
+      gf[s] = __builtin_bit_cast(bf16x8, gu);
+      const uint32_t ga[4] = {gu.x, gu.y, gu.z, gu.w}, oa[4] = {ou.x, ou.y, ou.z, ou.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dlt = fmaf(widen(ga[e] & 0xFFFFu), widen(oa[e] & 0xFFFFu), dlt);
+        dlt = fmaf(widen(ga[e] >> 16), widen(oa[e] >> 16), dlt);
+      }
     }
   }
-  const float lse2 = row_ok ? p.lse2[rowi] : INFINITY;
-  const float dlt = row_ok ? p.delta[rowi] : 0.f;
+  const float lse_in = row_ok ? p.lse[rowi] : -INFINITY;
   wait_vmcnt<0>();
+  dlt = group4_sum(dlt);
+  const float lse2 = lse_in == -INFINITY ? INFINITY : lse_in * 1.44269504088896340736f;
+  if (row_ok && g4 == 0) {  // for the dK/dV pass
+    p.delta[rowi] = dlt;
+    p.lse2[rowi] = lse2;
+  }
 #pragma unroll
   for (int s = 0; s < S::KS; ++s) launder(qf[s]);
 #pragma unroll
@@ -395,10 +390,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   {
     const uint16_t* krow = static_cast<const uint16_t*>(p.k) + keyi * D;
     const uint16_t* vrow = static_cast<const uint16_t*>(p.v) + keyi * Dv;
+    // The scale's sign goes on K here (S = (sign q) K^T = q (sign K)^T), so the
+    // streamed q fragments are used as they are.
+    const uint32_t kx = p.q_sign ? 0x80008000u : 0u;
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
       const int col = 32 * s + 8 * g4;
-      kf[s] = __builtin_bit_cast(bf16x8, (key_ok && col < D) ? load_u4(krow + col) : zero_u4());
+      kf[s] = neg_bf16x8(__builtin_bit_cast(bf16x8, (key_ok && col < D) ? load_u4(krow + col) : zero_u4()), kx);
     }
 #pragma unroll
     for (int s = 0; s < S::KSV; ++s) {
@@ -459,7 +457,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int j = 0; j < S::JV; ++j) accv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float c = p.scale_log2;
-  const uint32_t qx = p.q_sign ? 0x80008000u : 0u;
 
   auto body = [&](int r0, auto stg_tag, bool full) {
     constexpr int STG = decltype(stg_tag)::value;
@@ -484,7 +481,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int st = 0; st < S::KS; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = E::mfma(neg_bf16x8(tl.template a_frag<STG>(i, st), qx), kf[st], s[i]);
+      for (int i = 0; i < 4; ++i) s[i] = E::mfma(tl.template a_frag<STG>(i, st), kf[st], s[i]);
 #pragma unroll
     for (int st = 0; st < S::KSV; ++st)
 #pragma unroll
@@ -585,10 +582,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
       reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, true>),
   };
   if (rows > 0) {
-    const void* prep = p.f16 ? reinterpret_cast<const void*>(&bwd_prep_kernel<true>)
-                             : reinterpret_cast<const void*>(&bwd_prep_kernel<false>);
-    e = hipLaunchKernel(prep, dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, stream);
-    if (e != hipSuccess) return e;
     const int64_t n_qt = (p.Q + kBwdRows - 1) / kBwdRows;
     e = hipLaunchKernel(dq[sel], dim3((unsigned)(n_qt * p.Hq * p.B)), dim3(64 * kBwdWaves), args, 0, stream);
     if (e != hipSuccess) return e;
