@@ -185,8 +185,9 @@ def run_options(args, torch, af, inputs):
     (bf16 prefill, every key legal for every row), a paged K/V cache (pages of
     256 keys for the prefill, 128 for the decode, in random order), and two
     chunked-prefill shapes (short query runs against a long cache), heads of
-    256 channels on the step's two shapes and of 512 on the prefill shape, and
-    the backward at the prefill shape."""
+    256 channels on the step's two shapes and of 512 on the prefill shape, the
+    backward at the prefill shape, and the varlen windowed prefill and short
+    decode configurations."""
     import dataclasses
     c3, c5 = inputs.config(3), inputs.config(5)
     cases = [
@@ -207,6 +208,11 @@ def run_options(args, torch, af, inputs):
               ("prefill_d512", dataclasses.replace(c3, name="c3_shape_d512_prefill", D=512, Dv=512))]
     # The backward (attn_bwd) at the dense prefill shape.
     cases += [("backward", dataclasses.replace(c3, name="c3_shape_bf16_backward"))]
+    # The remaining configurations, reported beside the step: the
+    # variable-length windowed prefill (legal pairs from the realised lengths
+    # and the window) and the short decode with a ragged tail (latency-bound,
+    # its GB/s for information).
+    cases += [("prefill_varlen_window", inputs.config(4)), ("decode_tail", inputs.config(2))]
     hbm_bound = {"prefill_chunk64"}
     pages = {"prefill_paged": 256, "decode_paged": 128}
     stream = torch.cuda.current_stream()
