@@ -242,15 +242,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // Partial-state slot of this lane's row t in a split pass.
   auto part_slot = [&](int t) { return (int64_t)tile.part * kPrefillBM + (rw0 - tile.r0) + 16 * t + l16; };
 
-  // An empty piece of a split pass (past the end of this tile's range): its
-  // rows saw no key here.  The condition is uniform over the workgroup.
-  if (p.n_split > 1 && jb0 >= jb1) {
-    if (lead && wave_has_rows && g4 == 0) {
+  // A tile or piece with no key (an empty sequence, rows above a short
+  // sequence's first key, a piece past the end of the tile's range): its rows
+  // get O = 0 and LSE = -inf, or an empty partial state, without loading Q.
+  // The condition is uniform over the workgroup.
+  if (jb0 >= jb1) {
+    if (wave_has_rows) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (row_ok[t]) {
-          p.ws_m[part_slot(t)] = -INFINITY;
-          p.ws_l[part_slot(t)] = 0.f;
+        if (!row_ok[t]) continue;
+        if (p.n_split > 1) {
+          if (lead && g4 == 0) {
+            p.ws_m[part_slot(t)] = -INFINITY;
+            p.ws_l[part_slot(t)] = 0.f;
+          }
+        } else {
+          uint16_t* orow = static_cast<uint16_t*>(p.o) + row_index(t) * Dv_all + dv0;
+#pragma unroll
+          for (int j = 0; j < S::JV; ++j) {
+            const int dv = 16 * j + 4 * g4;
+            if (dv < Dv) *reinterpret_cast<ushort4*>(orow + dv) = ushort4{0, 0, 0, 0};
+          }
+          if (lead && g4 == 0) p.lse[row_index(t)] = -INFINITY;
         }
       }
     }
@@ -271,7 +284,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
       qf[t][s] = __builtin_bit_cast(bf16x8, u);
     }
   }
-  // Q is in registers before any direct load is issued.
+  // Q is in registers before any direct load is issued (issuing the first
+  // K/V block ahead of the Q loads measured no different, on the dense and
+  // on the windowed variable-length prefill).
   wait_vmcnt<0>();
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -558,16 +573,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     __syncthreads();
   };
 
-  if (jb0 < jb1) {
-    if (paged) {
-      pg_next = page_fetch(jb0);
-      wait_vmcnt<0>();
-    }
-    issue(jb0, 0, paged ? page_settle(pg_next) : 0);
-    if (paged) pg_next = page_fetch(jb0 + 1);
+  // Prologue (jb0 < jb1 here): the first block (its table entry first when
+  // the cache is paged).
+  if (paged) {
+    pg_next = page_fetch(jb0);
     wait_vmcnt<0>();
-    __syncthreads();
   }
+  issue(jb0, 0, paged ? page_settle(pg_next) : 0);
+  if (paged) pg_next = page_fetch(jb0 + 1);
+  wait_vmcnt<0>();
+  __syncthreads();
   for (int jb = jb0; jb < jb1; jb += 2) {
     block(jb, std::integral_constant<int, 0>{});
     if (jb + 1 < jb1) block(jb + 1, std::integral_constant<int, 1>{});
