@@ -437,3 +437,155 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   }
   return bad ? -3 : 0;
 }
+
+/*
+ * Backward on samples, for problems too large to differentiate in full on
+ * the host.  The same steps as oracle_attn_bwd, restricted:
+ *   oracle_attn_bwd_rows: dq of the listed flat rows (b*Hq+h)*Q+q, each from
+ *     its own row (weights, dP, delta, dS), into dq_out[i*D ...];
+ *   oracle_attn_bwd_keys: dk, dv of the listed flat keys (b*Hkv+kh)*K+k: every
+ *     row of the kv-head's query heads contributes through its full weights,
+ *     into dk_out[i*D ...] and dv_out[i*Dv ...].
+ * Returns 0 or a negative code as oracle_attn_fwd does.
+ */
+int oracle_attn_bwd_rows(const void* q, const void* k, const void* v, const void* dout, int dtype, const int64_t* rows,
+                         int64_t nrows, double* dq_out, int B, int Hq, int Hkv, int Q, int K, int D, int Dv,
+                         const int32_t* seqlens, int window, double scale, int threads, int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, dtype);
+  if (rc) return rc;
+  const int64_t total = (int64_t)B * Hq * Q;
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= total) return -1;
+  int bad = 0;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+  {
+    const size_t n = (size_t)(K > 0 ? K : 1);
+    double* scores = (double*)malloc(sizeof(double) * n);
+    unsigned char* lg = (unsigned char*)malloc(n);
+    double* pw = (double*)malloc(sizeof(double) * n);
+    double* dp = (double*)malloc(sizeof(double) * n);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nrows; ++i) {
+      if (!scores || !lg || !pw || !dp) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      const int64_t r = rows[i];
+      const int qi = (int)(r % Q), h = (int)((r / Q) % Hq), b = (int)(r / ((int64_t)Q * Hq));
+      const int kh = h / (Hq / Hkv);
+      const int64_t kbase = ((int64_t)b * Hkv + kh) * (int64_t)K;
+      double* dq = dq_out + i * D;
+      for (int d = 0; d < D; ++d) dq[d] = 0.0;
+      if (row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, causal, scale, D, D, b, h, qi, scores, lg) == 0)
+        continue;
+      double m = -INFINITY, l = 0.0, delta = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk)
+        if (lg[kk] && scores[kk] > m) m = scores[kk];
+      for (int64_t kk = 0; kk < K; ++kk)
+        if (lg[kk]) l += exp(scores[kk] - m);
+      for (int64_t kk = 0; kk < K; ++kk) {
+        if (!lg[kk]) continue;
+        pw[kk] = exp(scores[kk] - m) / l;
+        double acc = 0.0;
+        for (int j = 0; j < Dv; ++j)
+          acc += load_elem(dout, dtype, r * Dv + j) * load_elem(v, dtype, (kbase + kk) * Dv + j);
+        dp[kk] = acc;
+        delta += pw[kk] * acc;
+      }
+      for (int64_t kk = 0; kk < K; ++kk) {
+        if (!lg[kk]) continue;
+        const double ds = pw[kk] * (dp[kk] - delta);
+        for (int d = 0; d < D; ++d) dq[d] += scale * ds * load_elem(k, dtype, (kbase + kk) * D + d);
+      }
+    }
+    free(scores);
+    free(lg);
+    free(pw);
+    free(dp);
+  }
+  return bad ? -3 : 0;
+}
+
+int oracle_attn_bwd_keys(const void* q, const void* k, const void* v, const void* dout, int dtype, const int64_t* keys,
+                         int64_t nkeys, double* dk_out, double* dv_out, int B, int Hq, int Hkv, int Q, int K, int D,
+                         int Dv, const int32_t* seqlens, int window, double scale, int threads, int causal) {
+  int rc = check_args(B, Hq, Hkv, Q, K, D, Dv, seqlens, window, causal, dtype);
+  if (rc) return rc;
+  const int64_t total = (int64_t)B * Hkv * K;
+  for (int64_t i = 0; i < nkeys; ++i)
+    if (keys[i] < 0 || keys[i] >= total) return -1;
+  memset(dk_out, 0, sizeof(double) * (size_t)(nkeys * D));
+  memset(dv_out, 0, sizeof(double) * (size_t)(nkeys * Dv));
+  if (Hq == 0 || Q == 0) return 0;
+  const int g = Hq / Hkv;
+  int bad = 0;
+  /* One pass over the rows of each (b, kv-head) group that holds a listed key. */
+  for (int64_t gi = 0; gi < (int64_t)B * Hkv; ++gi) {
+    int any = 0;
+    for (int64_t i = 0; i < nkeys; ++i) any |= (keys[i] / K == gi);
+    if (!any) continue;
+    const int b = (int)(gi / Hkv), kh = (int)(gi % Hkv);
+    const int64_t kbase = gi * (int64_t)K;
+    const int64_t nrow = (int64_t)g * Q;
+#pragma omp parallel num_threads(threads > 0 ? threads : 1)
+    {
+      const size_t n = (size_t)(K > 0 ? K : 1);
+      double* scores = (double*)malloc(sizeof(double) * n);
+      unsigned char* lg = (unsigned char*)malloc(n);
+      double* pw = (double*)malloc(sizeof(double) * n);
+      double* dp = (double*)malloc(sizeof(double) * n);
+      double* tk = (double*)calloc((size_t)(nkeys * D + 1), sizeof(double));
+      double* tv = (double*)calloc((size_t)(nkeys * Dv + 1), sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t ri = 0; ri < nrow; ++ri) {
+        if (!scores || !lg || !pw || !dp || !tk || !tv) {
+#pragma omp atomic write
+          bad = 1;
+          continue;
+        }
+        const int h = kh * g + (int)(ri / Q), qi = (int)(ri % Q);
+        const int64_t r = ((int64_t)b * Hq + h) * Q + qi;
+        if (row_scores(q, k, dtype, Hq, Hkv, Q, K, D, seqlens, window, causal, scale, D, D, b, h, qi, scores, lg) ==
+            0)
+          continue;
+        double m = -INFINITY, l = 0.0, delta = 0.0;
+        for (int64_t kk = 0; kk < K; ++kk)
+          if (lg[kk] && scores[kk] > m) m = scores[kk];
+        for (int64_t kk = 0; kk < K; ++kk)
+          if (lg[kk]) l += exp(scores[kk] - m);
+        for (int64_t kk = 0; kk < K; ++kk) {
+          if (!lg[kk]) continue;
+          pw[kk] = exp(scores[kk] - m) / l;
+          double acc = 0.0;
+          for (int j = 0; j < Dv; ++j)
+            acc += load_elem(dout, dtype, r * Dv + j) * load_elem(v, dtype, (kbase + kk) * Dv + j);
+          dp[kk] = acc;
+          delta += pw[kk] * acc;
+        }
+        for (int64_t i = 0; i < nkeys; ++i) {
+          if (keys[i] / K != gi) continue;
+          const int64_t kk = keys[i] % K;
+          if (!lg[kk]) continue;
+          const double ds = pw[kk] * (dp[kk] - delta);
+          for (int j = 0; j < Dv; ++j) tv[i * Dv + j] += pw[kk] * load_elem(dout, dtype, r * Dv + j);
+          for (int d = 0; d < D; ++d) tk[i * D + d] += scale * ds * load_elem(q, dtype, r * D + d);
+        }
+      }
+#pragma omp critical
+      {
+        if (tk && tv) {
+          for (int64_t i = 0; i < nkeys * D; ++i) dk_out[i] += tk[i];
+          for (int64_t i = 0; i < nkeys * Dv; ++i) dv_out[i] += tv[i];
+        }
+      }
+      free(scores);
+      free(lg);
+      free(pw);
+      free(dp);
+      free(tk);
+      free(tv);
+    }
+  }
+  return bad ? -3 : 0;
+}

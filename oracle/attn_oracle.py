@@ -34,6 +34,12 @@ def _setup(lib):
     lib.oracle_attn_probs.restype = i64
     lib.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ci, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci, ci]
     lib.oracle_attn_bwd.restype = ci
+    lib.oracle_attn_bwd_rows.argtypes = [vp, vp, vp, vp, ci, vp, i64, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl, ci,
+                                         ci]
+    lib.oracle_attn_bwd_rows.restype = ci
+    lib.oracle_attn_bwd_keys.argtypes = [vp, vp, vp, vp, ci, vp, i64, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, dbl,
+                                         ci, ci]
+    lib.oracle_attn_bwd_keys.restype = ci
     return lib
 
 
@@ -186,3 +192,40 @@ class Oracle:
         if rc:
             raise OracleError(f"oracle_attn_bwd returned {rc}")
         return dq, dk, dv
+
+    def bwd_rows(self, q, k, v, dout, rows, *, seqlens=None, window=0, scale=None, threads=0, causal=True):
+        """dq of selected flat rows (b*Hq+h)*Q+q.  Returns [n, D] float64."""
+        B, Hq, Q, D = q.shape
+        _, Hkv, K, _ = k.shape
+        Dv = v.shape[-1]
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((len(r), D), dtype=np.float64)
+        sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
+        rc = self.lib.oracle_attn_bwd_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                           _dtype_code(q), r.ctypes.data, len(r), out.ctypes.data, B, Hq, Hkv, Q, K,
+                                           D, Dv, None if sl is None else sl.ctypes.data, int(window), float(scale),
+                                           _threads(threads), int(bool(causal)))
+        if rc:
+            raise OracleError(f"oracle_attn_bwd_rows returned {rc}")
+        return out
+
+    def bwd_keys(self, q, k, v, dout, keys, *, seqlens=None, window=0, scale=None, threads=0, causal=True):
+        """dk, dv of selected flat keys (b*Hkv+kh)*K+k.  Returns ([n, D], [n, Dv]) float64."""
+        B, Hq, Q, D = q.shape
+        _, Hkv, K, _ = k.shape
+        Dv = v.shape[-1]
+        if scale is None:
+            scale = 1.0 / np.sqrt(D)
+        kk = np.ascontiguousarray(keys, dtype=np.int64)
+        dk = np.empty((len(kk), D), dtype=np.float64)
+        dv = np.empty((len(kk), Dv), dtype=np.float64)
+        sl = None if seqlens is None else np.ascontiguousarray(seqlens, dtype=np.int32)
+        rc = self.lib.oracle_attn_bwd_keys(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                           _dtype_code(q), kk.ctypes.data, len(kk), dk.ctypes.data, dv.ctypes.data, B,
+                                           Hq, Hkv, Q, K, D, Dv, None if sl is None else sl.ctypes.data, int(window),
+                                           float(scale), _threads(threads), int(bool(causal)))
+        if rc:
+            raise OracleError(f"oracle_attn_bwd_keys returned {rc}")
+        return dk, dv

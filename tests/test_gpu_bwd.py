@@ -134,3 +134,45 @@ def test_bwd_backward_api(orc):
     for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         err = float(np.max(np.abs(g.float().cpu().numpy() - r)))
         assert err <= TOL * max(1.0, float(np.max(np.abs(r)))), (name, err)
+
+
+def test_bwd_full_dense_prefill_shape(orc):
+    """The backward at the dense prefill shape the bench times (B=4, Hq=32,
+    Hkv=8, Q=K=4096, D=Dv=128), on samples: dq of 256 rows (tile edges and
+    random ones) and dk/dv of 48 keys in three (batch, kv-head) groups, from
+    the oracle's sampled backward; every element written and finite."""
+    import torch
+    w = inputs.config(3)
+    say(f"[bwd] full {w.name} {w.shape_tuple}")
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    dout = inputs.normal(w.o_shape(), DOUT_ID, w.seed, "bf16")
+    tq, tk, tv, td = (to_dev(a) for a in (q, k, v, dout))
+    o, lse = af.forward(tq, tk, tv)
+    dq, dk, dv = af.backward(tq, tk, tv, o, lse, td)
+    torch.cuda.synchronize()
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all().item()), f"{name}: non-finite or unwritten elements"
+    rng = np.random.default_rng(3)
+    rows = set()
+    for qq in (0, 127, 128, 2047, 4095):
+        for b in range(w.B):
+            rows.add((b * w.Hq + int(rng.integers(w.Hq))) * w.Q + qq)
+    while len(rows) < 256:
+        rows.add(int(rng.integers(w.B * w.Hq * w.Q)))
+    rows = np.array(sorted(rows), np.int64)
+    keys = []
+    for gi in (0, 13, 31):
+        for kk in (0, 63, 64, 127, 128, 4032, 4095):
+            keys.append(gi * w.K + kk)
+        keys += [gi * w.K + int(x) for x in rng.integers(0, w.K, 9)]
+    keys = np.array(sorted(set(keys)), np.int64)
+    rq = orc.bwd_rows(q, k, v, dout, rows)
+    rk, rv = orc.bwd_keys(q, k, v, dout, keys)
+    gq = dq.float().cpu().numpy().reshape(-1, w.D)[rows]
+    gk = dk.float().cpu().numpy().reshape(-1, w.D)[keys]
+    gv = dv.float().cpu().numpy().reshape(-1, w.Dv)[keys]
+    for name, g, r in (("dq", gq, rq), ("dk", gk, rk), ("dv", gv, rv)):
+        err = float(np.max(np.abs(g - r)))
+        ref_max = float(np.max(np.abs(r)))
+        say(f"       {name}: err {err:.2e} (max|ref| {ref_max:.2e}, {len(r)} sampled)")
+        assert err <= TOL * max(1.0, ref_max), f"{name}: max abs err {err:.3e} vs max|ref| {ref_max:.3e}"

@@ -73,3 +73,43 @@ def test_config4_varlen_window(orc):
 
 def test_config5_long_decode(orc):
     _run_config(5, orc, 768)
+
+
+# The option workloads the bench times beside the step, at their full sizes,
+# on sampled rows: fp16 storage and the non-causal mode at the dense prefill
+# shape, heads of 256 and 512 channels there, the two chunked-prefill shapes
+# (packed tiles and split key ranges), fp16 storage at the long decode shape.
+def _run_option(w, orc, n_rows):
+    import dataclasses  # noqa: F401
+    say(f"[option] {w.name} {w.shape_tuple} {w.dtype} causal={w.causal} W={w.window}")
+    q = w.gen_q()
+    k = w.gen_k(padding="zero")
+    v = w.gen_v(padding="zero")
+    o, lse = run_gpu(w, q, k, v, check_inputs=False)
+    assert np.isfinite(o).all() and not np.isnan(lse).any()
+    rows = _sample_rows(w, n_rows)
+    ro, rl = orc.rows(q, k, v, rows, seqlens=w.seqlens, window=w.window, scale=w.scale, causal=w.causal)
+    return compare(o.reshape(-1, w.Dv)[rows], lse.reshape(-1)[rows], ro, rl, w.dtype, f"{w.name} ({len(rows)} rows)")
+
+
+def _c3(**kw):
+    import dataclasses
+    return dataclasses.replace(inputs.config(3), **kw)
+
+
+@pytest.mark.parametrize("variant", ["f16", "noncausal", "d256", "d512"])
+def test_option_dense_prefill_shape(orc, variant):
+    kw = {"f16": dict(name="c3_shape_f16", dtype="f16"), "noncausal": dict(name="c3_shape_noncausal", causal=False),
+          "d256": dict(name="c3_shape_d256", D=256, Dv=256), "d512": dict(name="c3_shape_d512", D=512, Dv=512)}
+    _run_option(_c3(**kw[variant]), orc, 256)
+
+
+@pytest.mark.parametrize("shape", [(4, 32, 8, 64, 16384, 128, 128), (1, 32, 8, 512, 32768, 128, 128)],
+                         ids=["chunk64_ctx16k", "chunk512_ctx32k"])
+def test_option_chunked_prefill(orc, shape):
+    _run_option(inputs.Workload("chunk", *shape), orc, 256)
+
+
+def test_option_long_decode_f16(orc):
+    import dataclasses
+    _run_option(dataclasses.replace(inputs.config(5), name="c5_shape_f16", dtype="f16"), orc, 512)

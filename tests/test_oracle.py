@@ -52,3 +52,23 @@ def test_oracle_bf16_inputs(orc):
     o2, l2 = orc.fwd(f(q), f(k), f(v))
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def test_oracle_bwd_samples_match_full(orc):
+    """The sampled backward (dq of chosen rows, dk/dv of chosen keys) equals the
+    full backward's entries."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, Q, K, D, Dv = 2, 6, 2, 9, 21, 16, 8
+    q = rng.standard_normal((B, Hq, Q, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, K, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, K, Dv)).astype(np.float32)
+    dout = rng.standard_normal((B, Hq, Q, Dv)).astype(np.float32)
+    for kw in (dict(seqlens=np.array([21, 6], np.int32), window=5), dict(causal=False)):
+        dq, dk, dv = orc.bwd(q, k, v, dout, **kw)
+        rows = np.array([0, 4, 17, 50, 107], np.int64)
+        np.testing.assert_allclose(orc.bwd_rows(q, k, v, dout, rows, **kw), dq.reshape(-1, D)[rows], rtol=0,
+                                   atol=1e-12)
+        keys = np.array([0, 3, 20, 22, 40, 83], np.int64)
+        sk, sv = orc.bwd_keys(q, k, v, dout, keys, **kw)
+        np.testing.assert_allclose(sk, dk.reshape(-1, D)[keys], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sv, dv.reshape(-1, Dv)[keys], rtol=0, atol=1e-12)
