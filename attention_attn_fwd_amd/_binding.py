@@ -224,7 +224,7 @@ def forward_paged(q, k_pages, v_pages, block_table, seqlens_k=None, window: int 
 def backward(q, k, v, o, lse, dout, seqlens_k=None, window: int = 0, scale: Optional[float] = None,
              stream=None, causal: bool = True):
     """Gradients of sum(dout * o) w.r.t. q, k, v on torch tensors (o and lse as the
-    forward returned them).  bfloat16 or float16, D and Dv up to 128.
+    forward returned them).  bfloat16 or float16, D and Dv up to 256.
     Returns (dq, dk, dv) in the input dtype."""
     import torch
 

@@ -310,7 +310,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   const int64_t rows = (int64_t)B * Hq * Q, keys = (int64_t)B * Hkv * K;
   if (rows == 0 && keys == 0) return ATTN_OK;
   if (flags & ATTN_FWD_FP32) return ATTN_ERR_UNSUPPORTED;
-  auto width_ok = [](int d) { return d >= 16 && d <= 128 && d % 16 == 0; };
+  auto width_ok = [](int d) { return d >= 16 && d <= 256 && d % 16 == 0; };
   if (!width_ok(D) || !width_ok(Dv)) return ATTN_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   if ((int64_t)Q * D * 2 >= lim || (int64_t)Q * Dv * 2 >= lim || (int64_t)K * D * 2 >= lim ||

@@ -64,7 +64,7 @@ struct BwdShape {
   static_assert(A_ROWS_PER_LOAD % (ACH < 16 ? ACH : 16) == 0 && B_ROWS_PER_LOAD % (BCH < 16 ? BCH : 16) == 0,
                 "a load round covers whole swizzle periods");
   static_assert(A_TILE + 48 * AROWB + 1024 < 65536 && B_TILE + 48 * BROWB + 1024 < 65536, "ds_read immediates");
-  static_assert(LDS <= 80 * 1024, "LDS");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Direct loads of two row tiles (A: width DP, B: width DVP) of kBwdBlock rows
@@ -153,10 +153,14 @@ __device__ __forceinline__ bf16x8 neg_bf16x8(bf16x8 x, uint32_t sign) {
 // dQ: workgroup = 128 query rows of head h of sequence b; wave w owns rows
 // 16w .. 16w + 15 (lane column l16).
 // ---------------------------------------------------------------------------
-// Two workgroups per CU (4 waves per SIMD, at most 128 VGPRs): 8% faster than
-// one on the dense prefill shape's backward.
+// Heads of exactly 64 or 128 channels: two workgroups per CU (4 waves per
+// SIMD, at most 128 VGPRs), 8% faster than one on the dense prefill shape's
+// backward.  Padded widths (their channel bounds take registers) and wider
+// heads (q, dO fragments and accumulators): one, without spills.
 template <int DP, int DVP, bool EXACT, bool F16>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(EXACT && DP <= 128 && DVP <= 128 ? 4 : 2,
+                                                                      EXACT && DP <= 128 && DVP <= 128 ? 4 : 2))) void
+bwd_dq_kernel(BwdParams p) {
   using S = BwdShape<DP, DVP>;
   using E = Elem<F16>;
   constexpr int BN = kBwdBlock;
@@ -353,8 +357,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // 16w .. 16w + 15 (lane column l16).  Streams 64-row blocks of q and dO of
 // the group's query heads, with the rows' lse2 and delta.
 // ---------------------------------------------------------------------------
-template <int DP, int DVP, bool EXACT, bool F16>
+// DK / DV select the outputs: both for heads up to 128; for wider heads one
+// launch each (dV needs only S and P; dK needs S, dP and dS), so a wave holds
+// one accumulator set.
+template <int DP, int DVP, bool EXACT, bool F16, bool DK, bool DV>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
+  static_assert(DK || DV, "an output");
   using S = BwdShape<DP, DVP>;
   using E = Elem<F16>;
   constexpr int BR = kBwdBlock;
@@ -401,14 +409,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S::KSV; ++s) {
       const int col = 32 * s + 8 * g4;
-      vf[s] = __builtin_bit_cast(bf16x8, (key_ok && col < Dv) ? load_u4(vrow + col) : zero_u4());
+      vf[s] = (DK && key_ok && col < Dv) ? __builtin_bit_cast(bf16x8, load_u4(vrow + col))
+                                         : __builtin_bit_cast(bf16x8, zero_u4());
     }
   }
   wait_vmcnt<0>();
 #pragma unroll
   for (int s = 0; s < S::KS; ++s) launder(kf[s]);
+  if constexpr (DK) {
 #pragma unroll
-  for (int s = 0; s < S::KSV; ++s) launder(vf[s]);
+    for (int s = 0; s < S::KSV; ++s) launder(vf[s]);
+  }
 
   // Rows that can see a key of this workgroup: position q + delta >= k0
   // (causal) and q + delta < k0 + 127 + W (window).
@@ -482,35 +493,42 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     for (int st = 0; st < S::KS; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[i] = E::mfma(tl.template a_frag<STG>(i, st), kf[st], s[i]);
+    if constexpr (DK) {
 #pragma unroll
-    for (int st = 0; st < S::KSV; ++st)
+      for (int st = 0; st < S::KSV; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dp[i] = E::mfma(tl.template b_frag<STG>(i, st), vf[st], dp[i]);
+        for (int i = 0; i < 4; ++i) dp[i] = E::mfma(tl.template b_frag<STG>(i, st), vf[st], dp[i]);
+    }
     // Rows 16i + 4*g4 + r: their lse2 and delta from LDS.
     f32x4 pw[4], ds[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t xa = xbase + STG * S::X_STAGE + (16 * i + 4 * g4) * 4;
       const f32x4 l2 = __builtin_bit_cast(f32x4, lds_read_b128(xa));
-      const f32x4 dl = __builtin_bit_cast(f32x4, lds_read_b128(xa + BR * 4));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pw[i][r] = fast_exp2(fmaf(s[i][r], c, -l2[r]));
-        ds[i][r] = pw[i][r] * (dp[i][r] - dl[r]);
+      for (int r = 0; r < 4; ++r) pw[i][r] = fast_exp2(fmaf(s[i][r], c, -l2[r]));
+      if constexpr (DK) {
+        const f32x4 dl = __builtin_bit_cast(f32x4, lds_read_b128(xa + BR * 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[i][r] = pw[i][r] * (dp[i][r] - dl[r]);
       }
     }
-    const bf16x8 pp0 = E::pack(pw[0], pw[1]), pp1 = E::pack(pw[2], pw[3]);
-    const bf16x8 dsp0 = E::pack(ds[0], ds[1]), dsp1 = E::pack(ds[2], ds[3]);
     // dV^T += dO^T P and dK^T += q^T dS over the block's two 32-row halves.
+    if constexpr (DV) {
+      const bf16x8 pp0 = E::pack(pw[0], pw[1]), pp1 = E::pack(pw[2], pw[3]);
 #pragma unroll
-    for (int j = 0; j < S::JV; ++j) {
-      accv[j] = E::mfma(tl.template b_tr<STG>(0, j), pp0, accv[j]);
-      accv[j] = E::mfma(tl.template b_tr<STG>(1, j), pp1, accv[j]);
+      for (int j = 0; j < S::JV; ++j) {
+        accv[j] = E::mfma(tl.template b_tr<STG>(0, j), pp0, accv[j]);
+        accv[j] = E::mfma(tl.template b_tr<STG>(1, j), pp1, accv[j]);
+      }
     }
+    if constexpr (DK) {
+      const bf16x8 dsp0 = E::pack(ds[0], ds[1]), dsp1 = E::pack(ds[2], ds[3]);
 #pragma unroll
-    for (int j = 0; j < S::JD; ++j) {
-      acck[j] = E::mfma(tl.template a_tr<STG>(0, j), dsp0, acck[j]);
-      acck[j] = E::mfma(tl.template a_tr<STG>(1, j), dsp1, acck[j]);
+      for (int j = 0; j < S::JD; ++j) {
+        acck[j] = E::mfma(tl.template a_tr<STG>(0, j), dsp0, acck[j]);
+        acck[j] = E::mfma(tl.template a_tr<STG>(1, j), dsp1, acck[j]);
+      }
     }
   };
 
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
   uint16_t* ko = static_cast<uint16_t*>(p.dk) + keyi * D;
   uint16_t* vo = static_cast<uint16_t*>(p.dv) + keyi * Dv;
 #pragma unroll
-  for (int j = 0; j < S::JD; ++j) {
+  for (int j = 0; j < (DK ? S::JD : 0); ++j) {
     const int d = 16 * j + 4 * g4;
     if (d < D) {
       ushort4 v4;
@@ -548,7 +566,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < S::JV; ++j) {
+  for (int j = 0; j < (DV ? S::JV : 0); ++j) {
     const int d = 16 * j + 4 * g4;
     if (d < Dv) {
       ushort4 v4;
@@ -575,12 +593,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
       reinterpret_cast<const void*>(&bwd_dq_kernel<DP, DVP, false, true>),
       reinterpret_cast<const void*>(&bwd_dq_kernel<DP, DVP, true, true>),
   };
-  const void* const dkdv[4] = {
-      reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, false>),
-      reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, false>),
-      reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, true>),
-      reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, true>),
-  };
   if (rows > 0) {
     const int64_t n_qt = (p.Q + kBwdRows - 1) / kBwdRows;
     e = hipLaunchKernel(dq[sel], dim3((unsigned)(n_qt * p.Hq * p.B)), dim3(64 * kBwdWaves), args, 0, stream);
@@ -588,11 +600,40 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   const int64_t n_kt = (p.K + kBwdRows - 1) / kBwdRows;
   if (n_kt == 0 || p.B == 0 || p.Hkv == 0) return hipSuccess;
-  return hipLaunchKernel(dkdv[sel], dim3((unsigned)(n_kt * p.Hkv * p.B)), dim3(64 * kBwdWaves), args, 0, stream);
+  const dim3 kgrid((unsigned)(n_kt * p.Hkv * p.B));
+  constexpr bool kSplit = DP > 128 || DVP > 128;  // dK and dV in separate launches
+  if constexpr (!kSplit) {
+    const void* const both[4] = {
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, false, true, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, false, true, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, true, true, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, true, true, true>),
+    };
+    return hipLaunchKernel(both[sel], kgrid, dim3(64 * kBwdWaves), args, 0, stream);
+  } else {
+    const void* const dk[4] = {
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, false, true, false>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, false, true, false>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, true, true, false>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, true, true, false>),
+    };
+    const void* const dv[4] = {
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, false, false, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, false, false, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, false, true, false, true>),
+        reinterpret_cast<const void*>(&bwd_dkdv_kernel<DP, DVP, true, true, false, true>),
+    };
+    e = hipLaunchKernel(dk[sel], kgrid, dim3(64 * kBwdWaves), args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel(dv[sel], kgrid, dim3(64 * kBwdWaves), args, 0, stream);
+  }
 }
 
+// Heads up to 128 wide on kernels sized for them; wider (up to 256) padded to
+// 256 on both sides.
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const int dp = pad_width(p.D), dvp = pad_width(p.Dv);
+  if (dp > 128 || dvp > 128) return launch_bwd_t<256, 256>(p, stream);
   if (dp == 64 && dvp == 64) return launch_bwd_t<64, 64>(p, stream);
   if (dp == 64 && dvp == 128) return launch_bwd_t<64, 128>(p, stream);
   if (dp == 128 && dvp == 64) return launch_bwd_t<128, 64>(p, stream);

@@ -207,7 +207,8 @@ def run_options(args, torch, af, inputs):
               ("decode_d256", dataclasses.replace(c5, name="c5_shape_d256_decode", D=256, Dv=256)),
               ("prefill_d512", dataclasses.replace(c3, name="c3_shape_d512_prefill", D=512, Dv=512))]
     # The backward (attn_bwd) at the dense prefill shape.
-    cases += [("backward", dataclasses.replace(c3, name="c3_shape_bf16_backward"))]
+    cases += [("backward", dataclasses.replace(c3, name="c3_shape_bf16_backward")),
+              ("backward_d256", dataclasses.replace(c3, name="c3_shape_d256_backward", D=256, Dv=256))]
     # The remaining configurations, reported beside the step: the
     # variable-length windowed prefill (legal pairs from the realised lengths
     # and the window) and the short decode with a ragged tail (latency-bound,
@@ -221,7 +222,7 @@ def run_options(args, torch, af, inputs):
         pr = Problem(w, torch)
         if tag in pages:
             pr.paginate(pages[tag], torch)
-        if tag == "backward":
+        if tag.startswith("backward"):
             pr.make_backward(af, torch)
         for _ in range(args.warmup):
             pr.call(af, stream)
@@ -233,7 +234,7 @@ def run_options(args, torch, af, inputs):
         ev[args.steps].record(stream)
         torch.cuda.synchronize()
         t = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])) * 1e-3
-        if (tag.startswith("prefill") or tag == "backward") and tag not in hbm_bound:
+        if (tag.startswith("prefill") or tag.startswith("backward")) and tag not in hbm_bound:
             achieved, peak, unit, bound = pr.flops / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = pr.kv_bytes / t / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"

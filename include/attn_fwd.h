@@ -152,7 +152,8 @@ int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void
  * stream-ordered pool as the forward's.
  *
  * Returns as attn_fwd_ex, and ATTN_ERR_UNSUPPORTED for ATTN_FWD_FP32 or D, Dv
- * outside multiples of 16 in [16, 128].
+ * outside multiples of 16 in [16, 256] (above 128, dK and dV are computed by
+ * separate launches, each recomputing the weights).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
              void* dk, void* dv, int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens_k,

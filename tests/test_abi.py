@@ -223,8 +223,8 @@ def test_bwd_argument_checks():
     assert bwd(dk=None) == bad
     assert bwd(q=fake + 2) == bad
     assert bwd(flags=af.ATTN_FWD_FP32) == uns
-    assert bwd(D=256) == uns
-    assert bwd(Dv=144) == uns
+    assert bwd(D=272) == uns
+    assert bwd(Dv=512) == uns
     assert bwd(D=72) == uns
     assert bwd(K=1 << 23, D=128) == uns
     assert bwd(B=0) == af.ATTN_OK

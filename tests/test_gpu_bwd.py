@@ -97,6 +97,27 @@ def test_bwd_shapes(orc, shape, dtype, causal):
     _check(orc, inputs.Workload("bwd", *shape, dtype=dtype, causal=causal))
 
 
+# Heads wider than 128 (up to 256, padded to 256): dK and dV in separate
+# launches, one dQ workgroup per CU.
+WIDE = [
+    (1, 4, 2, 64, 128, 256, 256),
+    (2, 8, 2, 200, 300, 256, 256),
+    (1, 8, 2, 1, 999, 192, 256),
+    (1, 4, 4, 130, 90, 256, 128),
+    (2, 4, 2, 65, 131, 144, 80),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_wide_heads(orc, shape, dtype, causal):
+    _check(orc, inputs.Workload("bwd_wide", *shape, dtype=dtype, causal=causal))
+    if causal and shape[0] > 1:
+        sl = np.array([shape[4], 0][:shape[0]], np.int32)
+        _check(orc, inputs.Workload("bwd_wide_varlen", *shape, dtype=dtype, seqlens=sl), window=33, tag=" W=33")
+
+
 @pytest.mark.parametrize("window", [1, 17, 64, 200])
 def test_bwd_window(orc, window):
     sl = np.array([333, 0, 100], np.int32)
