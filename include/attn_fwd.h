@@ -1,6 +1,6 @@
 /*
  * attn_fwd.h - C ABI of libattn_fwd.so: causal grouped-query attention
- * forward on AMD Instinct MI355X (gfx950).
+ * forward (and its backward, attn_bwd) on AMD Instinct MI355X (gfx950).
  *
  * The operation is the attention fixture of the LuisaCompute "Attention
  * execution mapping" review, section 1: bottom-right causal GQA in which
