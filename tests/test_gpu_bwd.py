@@ -197,3 +197,44 @@ def test_bwd_full_dense_prefill_shape(orc):
         ref_max = float(np.max(np.abs(r)))
         say(f"       {name}: err {err:.2e} (max|ref| {ref_max:.2e}, {len(r)} sampled)")
         assert err <= TOL * max(1.0, ref_max), f"{name}: max abs err {err:.3e} vs max|ref| {ref_max:.3e}"
+
+
+def test_bwd_forced_scratch_failure_reports_oom():
+    """A failed scratch allocation is reported; nothing is written."""
+    import os
+    import torch
+    w = inputs.Workload("bwd_oom", 1, 4, 2, 40, 100, 64, 64)
+    q, k, v = (to_dev(a) for a in (w.gen_q(), w.gen_k(), w.gen_v()))
+    o, lse = af.forward(q, k, v)
+    dout = to_dev(inputs.normal(w.o_shape(), DOUT_ID, w.seed, "bf16"))
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    os.environ["ATTN_FWD_FAIL_ALLOC"] = "1"
+    try:
+        st = af.attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Q, w.K, w.D, w.Dv, None, 0, w.scale,
+                         0, torch.cuda.current_stream())
+    finally:
+        del os.environ["ATTN_FWD_FAIL_ALLOC"]
+    torch.cuda.synchronize()
+    assert st == af.ATTN_ERR_OOM
+    for t in (dq, dk, dv):
+        assert torch.isnan(t.float()).all()
+
+
+def test_bwd_side_stream(orc):
+    """The backward on a side stream, waited on by the default stream."""
+    import torch
+    w = inputs.Workload("bwd_stream", 2, 8, 2, 130, 700, 128, 128, seqlens=np.array([700, 301], np.int32))
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    dout = inputs.normal(w.o_shape(), DOUT_ID, w.seed, "bf16")
+    tq, tk, tv, td, sl = (to_dev(a) for a in (q, k, v, dout, w.seqlens))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o, lse = af.forward(tq, tk, tv, seqlens_k=sl, stream=side)
+        dq, dk, dv = af.backward(tq, tk, tv, o, lse, td, seqlens_k=sl, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    refs = orc.bwd(q, k, v, dout, seqlens=w.seqlens)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = float(np.max(np.abs(g.float().cpu().numpy() - r)))
+        assert err <= TOL * max(1.0, float(np.max(np.abs(r)))), (name, err)
