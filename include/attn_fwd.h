@@ -47,6 +47,13 @@
  * seqlens_k is never read on the host.  Values outside [0, K] are a caller
  * error; the kernels clamp them to [0, K] so memory outside the tensors is
  * never touched.
+ *
+ * Environment (read at each call; for tests and tuning, not needed in use):
+ *   ATTN_FWD_SPLIT_WORKERS=n   workers of the split-KV decode pass (n >= 1);
+ *   ATTN_FWD_PREFILL_SPLITS=n  key-range pieces per prefill tile (n >= 1,
+ *                              at most 32; rounded to whole pieces);
+ *   ATTN_FWD_FAIL_ALLOC=1      every scratch allocation fails (the calls
+ *                              that need scratch return ATTN_ERR_OOM).
  */
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
