@@ -46,6 +46,16 @@ def load():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_attn_fwd_amd.build` "
                               "(there is no fallback path)")
+        # One HIP runtime per process: PyTorch ships its own libamdhip64 and
+        # loads it by a name that does not match a runtime already mapped from
+        # ROCm's lib directory, so loading the library first would leave two
+        # runtimes side by side (the second one's launches can fail with
+        # hipErrorNoDevice).  Loaded after torch, the library's dependency
+        # resolves by soname to torch's copy.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         sig = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, cf, vp]
