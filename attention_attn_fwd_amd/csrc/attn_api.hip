@@ -141,7 +141,8 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
       (int64_t)K * Dv * 2 >= lim)
     return ATTN_ERR_UNSUPPORTED;
   const int group = Hq / Hkv;
-  if (bf16 && Q <= kDecodeMaxQ && group * Q <= kDecodeMaxRows && D <= 128 && Dv <= 128) {
+  const bool narrow = D <= 128 && Dv <= 128, wide = !narrow && D <= 256 && Dv <= 256;
+  if (bf16 && Q <= kDecodeMaxQ && ((narrow && group * Q <= kDecodeMaxRows) || (wide && group * Q <= kDecodeMaxRowsWide))) {
     plan->path = 2;
     plan->split_workers = split_workers(B, Hkv, K, D, Dv, group * Q);
     plan->partial_slots = plan->split_workers > 0 ? B * Hkv + plan->split_workers : 0;

@@ -52,6 +52,9 @@ constexpr int kDecodeMaxRows = 32;  // g*Q rows packed per (batch, kv-head)
 // (decode Q = 1..4, and the short query runs of speculative decoding or
 // chunked prefill): the packed rows share each K/V read.
 constexpr int kDecodeMaxQ = kDecodeMaxRows;
+// Heads wider than 128 (up to 256) take the split-KV path only up to this many
+// packed rows (one 16-row MFMA tile).
+constexpr int kDecodeMaxRowsWide = 16;
 // Each worker of the split pass takes at least kDecodeMinShare sub-blocks.
 constexpr int kDecodeMinShare = 4;
 

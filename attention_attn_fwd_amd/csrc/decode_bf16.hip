@@ -297,6 +297,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     // Every LDS read of the sub-block is issued up front (K fragments, then the
     // transposed V fragments), so a single wave pays the LDS latency once per
     // step rather than once per fragment; the V reads overlap QK and softmax.
+    // Heads wider than 128: the V fragments are read after the softmax, once
+    // the K fragments are dead (both sets at once would not fit the registers).
+    constexpr bool kLateV = DP > 128 || DVP > 128;
     bf16x8 kf[2][S::KS];
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
@@ -310,14 +313,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     // 16 + 4*g4 + e - 4, the S^T register layout; each is two transposed reads
     // of 4-row pieces of the swizzled V tile.
     bf16x8 vf[S::JV];
+    if constexpr (!kLateV) {
 #pragma unroll
-    for (int jv = 0; jv < S::JV; ++jv) {
-      const int row = 4 * g4 + (l16 >> 2);
-      const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
-      const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
-      const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
-      vf[jv] = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
-                             lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
+      for (int jv = 0; jv < S::JV; ++jv) {
+        const int row = 4 * g4 + (l16 >> 2);
+        const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+        const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
+        const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
+        vf[jv] = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
+                               lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -379,6 +384,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
       pf[t] = E::pack(sacc[0][t], sacc[1][t]);
     }
     // O^T += V^T P^T.
+    if constexpr (kLateV) {
+#pragma unroll
+      for (int jv = 0; jv < S::JV; ++jv) {
+        const int row = 4 * g4 + (l16 >> 2);
+        const int ch = 2 * jv + ((l16 & 3) >> 1), half = (l16 & 1) * 8;
+        const unsigned char* lo = vst + row * S::VROWB + ((ch ^ swz_v<S::VCH>(row)) << 4) + half;
+        const unsigned char* hi = vst + (row + 16) * S::VROWB + ((ch ^ swz_v<S::VCH>(row + 16)) << 4) + half;
+        vf[jv] = concat_bf16x4(lds_read_tr16(reinterpret_cast<const uint16_t*>(lo)),
+                               lds_read_tr16(reinterpret_cast<const uint16_t*>(hi)));
+      }
+    }
 #pragma unroll
     for (int jv = 0; jv < S::JV; ++jv)
 #pragma unroll
@@ -423,9 +439,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
 // order.  The pieces of group g were made by workers first..last of the same
 // partition (recomputed here) and sit at slots g + w.  Pieces are taken eight
 // at a time: every lane loads the eight pieces' (m, l) (the same addresses in
-// every lane) and its two dv columns of each, all in one round of loads, and
-// folds them into a running (M, L, o) that is rescaled when M moves, so a row
-// with at most eight pieces costs one round trip to memory.
+// every lane) and its NC dv columns of each (lane + 64c), all in one round of
+// loads, and folds them into a running (M, L, o) that is rescaled when M
+// moves, so a row with at most eight pieces costs one round trip to memory.
+template <int NC>
 __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row_id = (int64_t)blockIdx.x * 4 + wave;
@@ -453,19 +470,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
 
   // Running merge; a piece with no legal key for this row has m = -inf and
   // contributes nothing.
-  float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
+  float M = -INFINITY, L = 0.f, o[NC] = {};
   constexpr int U = 8;
   for (int w0 = w_first; w0 <= w_last; w0 += U) {
-    float m[U], l[U], a0[U], a1[U];
+    float m[U], l[U], a[U][NC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = w0 + u <= w_last;
       const int64_t sp = (g + w0 + u) * R + rr;
-      const float* a = p.ws_acc + sp * p.Dv;
+      const float* ap = p.ws_acc + sp * p.Dv;
       m[u] = ok ? p.ws_m[sp] : -INFINITY;
       l[u] = ok ? p.ws_l[sp] : 0.f;
-      a0[u] = ok && lane < p.Dv ? a[lane] : 0.f;
-      a1[u] = ok && lane + 64 < p.Dv ? a[lane + 64] : 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) a[u][cc] = ok && lane + 64 * cc < p.Dv ? ap[lane + 64 * cc] : 0.f;
     }
     float mc = m[0];
 #pragma unroll
@@ -474,22 +491,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(Params p) {
     const float mn = fmaxf(M, mc);
     const float alpha = M == -INFINITY ? 0.f : fast_exp2(M - mn);
     L *= alpha;
-    o0 *= alpha;
-    o1 *= alpha;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) o[cc] *= alpha;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float f = m[u] == -INFINITY ? 0.f : fast_exp2(m[u] - mn);
       L = fmaf(l[u], f, L);
-      o0 = fmaf(a0[u], f, o0);
-      o1 = fmaf(a1[u], f, o1);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) o[cc] = fmaf(a[u][cc], f, o[cc]);
     }
     M = mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(p.o) + row_id * p.Dv;
   auto cvt = [&](float x) { return p.f16 ? Elem<true>::cvt(x) : Elem<false>::cvt(x); };
-  if (lane < p.Dv) orow[lane] = cvt(o0 * inv);
-  if (lane + 64 < p.Dv) orow[lane + 64] = cvt(o1 * inv);
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+    if (lane + 64 * cc < p.Dv) orow[lane + 64 * cc] = cvt(o[cc] * inv);
   if (lane == 0) p.lse[row_id] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
 }
 
@@ -506,7 +524,9 @@ static hipError_t launch_decode_t(const Params& p, hipStream_t stream) {
   }
   const int64_t rows = (int64_t)p.B * p.Hq * p.Q;
   const dim3 cgrid((unsigned)((rows + 3) / 4));
-  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel), cgrid, dim3(256), args, 0, stream);
+  constexpr int NC = DVP <= 128 ? 2 : 4;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel<NC>), cgrid, dim3(256), args, 0,
+                         stream);
 }
 
 template <int DP, int DVP>
@@ -515,8 +535,11 @@ static hipError_t launch_decode_nt(const Params& p, hipStream_t stream) {
   return launch_decode_t<DP, DVP, 2>(p, stream);
 }
 
+// Heads up to 128 on kernels sized for them; up to 256 (padded to 256 on both
+// sides) for at most 16 packed rows (the plan sends more to the prefill kernel).
 hipError_t launch_decode_bf16(const Params& p, hipStream_t stream) {
   const int dp = pad_width(p.D), dvp = pad_width(p.Dv);
+  if (dp > 128 || dvp > 128) return launch_decode_t<256, 256, 1>(p, stream);
   if (dp == 64 && dvp == 64) return launch_decode_nt<64, 64>(p, stream);
   if (dp == 64 && dvp == 128) return launch_decode_nt<64, 128>(p, stream);
   if (dp == 128 && dvp == 64) return launch_decode_nt<128, 64>(p, stream);

@@ -28,6 +28,19 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, name), name
 
 
+def test_one_hip_runtime_in_the_process():
+    """Loading the library (before anything imported torch) must leave a single
+    libamdhip64 mapped: the one torch uses, which the library binds to."""
+    import subprocess
+    import sys
+    code = ("import attention_attn_fwd_amd as af; af._binding.load(); import torch; "
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1"
+
+
 def test_strerror():
     for st in range(5):
         assert af.strerror(st)
@@ -66,10 +79,19 @@ def test_wide_heads_only_on_the_16bit_path():
     for D, Dv in [(256, 256), (144, 64), (64, 256), (512, 512), (512, 64), (400, 272)]:
         st = af.attn_fwd_f32(fake, fake, fake, fake, fake, 1, 4, 2, 8, 8, D, Dv, None, 0, 1.0, None)
         assert st == af.ATTN_ERR_UNSUPPORTED, (D, Dv)
-        assert af.attn_fwd_plan(1, 4, 2, 8, 8, D, Dv)["path"] == af.PATH_PREFILL
-    # Every Q of a wide head takes the prefill kernel (no decode kernel that wide).
-    assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 256, 256)["path"] == af.PATH_PREFILL
+        # 16 packed rows: the decode kernel up to 256 channels, else prefill.
+        want = af.PATH_DECODE if max(D, Dv) <= 256 else af.PATH_PREFILL
+        assert af.attn_fwd_plan(1, 4, 2, 8, 8, D, Dv)["path"] == want, (D, Dv)
+    # Heads of 129..256 channels decode on the split-KV kernel up to 16 packed
+    # rows; more rows, or heads above 256, take the prefill kernel.
+    assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 256, 256)["path"] == af.PATH_DECODE
+    assert af.attn_fwd_plan(8, 32, 2, 1, 4096, 256, 256)["path"] == af.PATH_DECODE   # 16 rows
+    assert af.attn_fwd_plan(8, 34, 2, 1, 4096, 256, 256)["path"] == af.PATH_PREFILL  # 17 rows
+    assert af.attn_fwd_plan(8, 8, 2, 5, 4096, 256, 256)["path"] == af.PATH_PREFILL   # 20 rows
+    assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 512, 512)["path"] == af.PATH_PREFILL
     assert af.attn_fwd_plan(8, 8, 2, 1, 4096, 128, 128)["path"] == af.PATH_DECODE
+    # Two 40 KiB ring stages of 256-channel K, V and Q: two workers per CU.
+    assert af.attn_fwd_plan(64, 64, 8, 1, 32768, 256, 256)["split_workers"] == 512
 
 
 @pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
@@ -190,10 +212,10 @@ def test_plan_prefill_splits(monkeypatch):
     assert af.attn_fwd_plan(1, 4, 2, 65, 0, 64, 64)["split_workers"] == 1
     # At most 32 pieces; the override is clamped the same way.
     assert af.attn_fwd_plan(1, 1, 1, 128, 1 << 20, 64, 64)["split_workers"] == 32
-    # Lean tiles (decode with wide heads: 8 packed rows) over long keys:
+    # Lean tiles (decode with wide heads: 32 packed rows) over long keys:
     # pieces of 32 blocks whatever the tile count.
-    assert af.attn_fwd_plan(64, 64, 8, 1, 32768, 256, 256)["split_workers"] == 16
-    assert af.attn_fwd_plan(64, 64, 8, 1, 2047, 256, 256)["split_workers"] == 1
+    assert af.attn_fwd_plan(128, 128, 4, 1, 32768, 256, 256)["split_workers"] == 16
+    assert af.attn_fwd_plan(128, 128, 4, 1, 2047, 256, 256)["split_workers"] == 1
     # Pieces hold a fixed number of blocks: a count is rounded to what whole
     # pieces of ceil(blocks / count) blocks need.
     monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", "7")

@@ -135,14 +135,19 @@ def test_prefill_forced_splits(orc, shape, splits, monkeypatch):
     _check(w, orc=orc, tag=f" splits={splits}")
 
 
-# Heads wider than 128 (up to 256): the 8-wave prefill form, for every Q
-# (decode shapes included: packed rows and split key ranges), padded widths
-# (D or Dv below 256), D != Dv, causal and not, windows, empty sequences.
+# Heads wider than 128 (up to 256): the 8-wave prefill form (decode shapes
+# of more than 16 packed rows included: split key ranges) and the split-KV
+# decode kernel up to 16 rows; padded widths (D or Dv below 256), D != Dv,
+# causal and not, windows, empty sequences.
 WIDE = [
     (1, 4, 2, 64, 128, 256, 256),
     (2, 8, 2, 300, 700, 256, 256),
-    (1, 8, 2, 1, 2053, 256, 256),     # decode: 8 packed rows, split keys
-    (2, 16, 8, 3, 999, 256, 256),
+    (1, 8, 2, 1, 2053, 256, 256),     # decode kernel: 4 packed rows
+    (2, 16, 8, 3, 999, 256, 256),     # decode kernel: 6 rows
+    (1, 32, 1, 1, 2053, 256, 256),    # prefill kernel: 32 packed rows, split keys
+    (2, 4, 1, 4, 3000, 256, 256),     # decode kernel: 16 rows
+    (3, 4, 2, 7, 1111, 192, 256),     # decode kernel: 14 rows, D padded
+    (1, 2, 2, 5, 777, 256, 64),       # decode kernel: Dv padded
     (2, 16, 8, 200, 333, 192, 256),
     (1, 4, 4, 130, 90, 256, 128),     # more rows than keys, Dv padded
     (1, 4, 2, 65, 131, 144, 80),
@@ -154,7 +159,9 @@ WIDE = [
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", WIDE, ids=lambda s: "x".join(map(str, s)))
 def test_wide_heads(orc, shape, dtype, causal):
-    assert af.attn_fwd_plan(*shape)["path"] == af.PATH_PREFILL
+    B, Hq, Hkv, Q = shape[:4]
+    want = af.PATH_DECODE if Hq // Hkv * Q <= 16 else af.PATH_PREFILL
+    assert af.attn_fwd_plan(*shape)["path"] == want
     w = inputs.Workload("wide", *shape, dtype=dtype, causal=causal)
     _check(w, orc=orc)
     B = shape[0]
@@ -424,6 +431,24 @@ def test_decode_partitions(orc, workers, Q, window):
     sl[[0, 5, 6]] = [0, 1, 2]
     sl[[10, 11]] = [700, 33]
     w = inputs.Workload("partitions", 24, 16, 4, Q, 700, 64, 64, seqlens=sl, window=window)
+    os.environ["ATTN_FWD_SPLIT_WORKERS"] = str(workers)
+    try:
+        _check(w, orc=orc, tag=f" workers={workers}")
+    finally:
+        del os.environ["ATTN_FWD_SPLIT_WORKERS"]
+
+
+@pytest.mark.parametrize("workers", [1, 7, 300, 4096])
+@pytest.mark.parametrize("Q,window", [(1, 0), (2, 0), (1, 50), (4, 97)])
+def test_decode_partitions_wide(orc, workers, Q, window):
+    """The split-KV decode kernel at 256 channels (V fragments read after the
+    softmax, four output columns a lane in the combine): shares that split
+    sequences anywhere, empty and tiny ones, D != Dv."""
+    rng = np.random.default_rng(11)
+    sl = rng.integers(0, 900, size=6).astype(np.int32)
+    sl[[0, 1]] = [0, 1]
+    w = inputs.Workload("partitions_wide", 6, 8, 2, Q, 900, 256, 208, seqlens=sl, window=window)
+    assert af.attn_fwd_plan(6, 8, 2, Q, 900, 256, 208)["path"] == af.PATH_DECODE
     os.environ["ATTN_FWD_SPLIT_WORKERS"] = str(workers)
     try:
         _check(w, orc=orc, tag=f" workers={workers}")
