@@ -37,8 +37,10 @@
  * streams do not share scratch.
  *
  * Head widths: D and Dv up to 128 run on kernels sized for them; wider
- * heads run on 8-wave forms of the prefill kernel for every Q, decode
- * included: up to 256 with two 64-key K/V blocks resident, up to 512 with
+ * heads run on 8-wave forms of the prefill kernel (decode with more than 16
+ * packed rows g*Q included; up to 16 such rows of heads up to 256 take the
+ * split-KV decode kernel padded to 256): up to 256 with two 64-key K/V
+ * blocks resident, up to 512 with
  * 32-key blocks and the output channels in parts of 256 on separate
  * workgroups that each recompute the scores (the FlyDSL post, "FMHA through
  * AOTriton", gives 512 a body of its own for the same LDS reason: two
