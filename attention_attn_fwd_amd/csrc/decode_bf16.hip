@@ -1,4 +1,6 @@
-// Split-KV decode for Q = 1..4 on gfx950, plus the log-sum-exp combine pass.
+// Split-KV decode on gfx950 (short query runs: up to 32 packed rows g*Q for
+// heads up to 128 channels, up to 16 for heads up to 256), plus the
+// log-sum-exp combine pass.
 //
 // The recurrence is the one of the LuisaCompute "Attention execution mapping"
 // review, section 1 (online (row_max, row_sum, acc) carried across KV
