@@ -19,7 +19,8 @@
 //     for a dispatch: with one workgroup per fixed-size chunk, a batch of
 //     uneven lengths left the GPU half idle for the last third of the pass;
 //   * a worker streams through a two-stage LDS ring of sub-blocks filled by
-//     direct buffer-to-LDS loads; the sub-block that opens a group in the
+//     direct buffer-to-LDS loads (K and V with the non-temporal hint: each
+//     byte is read once); the sub-block that opens a group in the
 //     worker's share also carries that group's Q rows in its stage, so the Q
 //     of the next group arrives in order with its keys; rows past K_b and
 //     channels past D read as zero from the buffer range check;
@@ -224,9 +225,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(Params p) {
     const rsrc_t vrs = slice_rsrc(sp.v, rows_left * p.Dv * 2);
     const uint32_t st = ring0 + stg * S::STAGE;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) load_lds16(krs, st + i * 1024, koff[i]);
+    for (int i = 0; i < S::K_LOADS; ++i) load_lds16_nt(krs, st + i * 1024, koff[i]);
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) load_lds16(vrs, st + S::K_STAGE + i * 1024, voff[i]);
+    for (int i = 0; i < S::V_LOADS; ++i) load_lds16_nt(vrs, st + S::K_STAGE + i * 1024, voff[i]);
     if (with_q) {
       const rsrc_t qrs = slice_rsrc(
           static_cast<const uint16_t*>(p.q) + ((int64_t)c.b * p.Hq + c.kh * p.group) * p.Q * p.D, (uint32_t)R * p.D * 2);
