@@ -4,6 +4,9 @@
                      (csrc/*.hip, compiled with hipcc, one object per source,
                      in parallel, then linked)
   libattn_inputs.so  the seeded input generator (csrc/inputs.c, gcc + OpenMP)
+  libattn_calib.so   a kernel of known MFMA count that calibrates the
+                     hardware counters the benchmark reads (csrc/calib.hip;
+                     loaded only by bench.py --workload mfma_cal)
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
 off (-Xclang -target-feature -Xclang -packed-fp32-ops) and with MFMA results
@@ -23,6 +26,7 @@ ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn_fwd.so")
 INPUTS_LIB = os.path.join(HERE, "libattn_inputs.so")
+CALIB_LIB = os.path.join(HERE, "libattn_calib.so")
 ARCH = os.environ.get("ATTN_FWD_ARCH", "gfx950")
 
 HIP_SOURCES = ["attn_api.hip", "prefill_bf16.hip", "decode_bf16.hip", "fwd_f32.hip", "bwd_bf16.hip"]
@@ -80,8 +84,19 @@ def build_inputs() -> str:
     return INPUTS_LIB
 
 
+def build_calib() -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    obj = os.path.join(BUILD_DIR, "calib.o")
+    _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", obj])
+    tmp = CALIB_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj])
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
+
+
 def build_all(verbose: bool = False) -> list[str]:
-    return [build_inputs(), build_lib(verbose=verbose)]
+    return [build_inputs(), build_lib(verbose=verbose), build_calib()]
 
 
 if __name__ == "__main__":

@@ -46,6 +46,47 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   return dp.err;
 }
 
+// Chip geometry, queried once per device: compute units and XCDs (the
+// partition mode decides both; a single-XCD partition has no XCD mapping).
+// ATTN_FWD_CUS / ATTN_FWD_XCDS override them (tests plan for other chips on
+// hosts without a GPU); with no device the MI355X figures stand in.
+struct Geometry {
+  int cus = 256;
+  int xcds = 8;
+};
+struct GeometrySlot {
+  std::once_flag once;
+  Geometry g;
+};
+GeometrySlot g_geometry[kMaxDevices];
+
+Geometry device_geometry() {
+  Geometry g;
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+    GeometrySlot& gs = g_geometry[dev];
+    std::call_once(gs.once, [&]() {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) gs.g.cus = v;
+      v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) gs.g.xcds = v;
+      (void)hipGetLastError();
+    });
+    g = gs.g;
+  } else {
+    (void)hipGetLastError();
+  }
+  if (const char* e = std::getenv("ATTN_FWD_CUS")) {
+    const int v = std::atoi(e);
+    if (v >= 1) g.cus = v;
+  }
+  if (const char* e = std::getenv("ATTN_FWD_XCDS")) {
+    const int v = std::atoi(e);
+    if (v >= 1) g.xcds = v;
+  }
+  return g;
+}
+
 // A failed launch is reported through the status code; the runtime's
 // per-thread error state it set is consumed so it does not surface later in
 // the caller's unrelated HIP calls.
@@ -62,38 +103,40 @@ bool supported_width(int d, bool mfma) { return d >= 16 && d <= (mfma ? 512 : 12
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Workers of the split-KV pass: as many single-wave workgroups as are
-// resident at once (four per CU of the 256, fewer when the two LDS ring
-// stages of K, V and Q sub-blocks need more than 40 KiB), fewer still when
-// even the padded length gives less than kDecodeMinShare sub-blocks each.
-// ATTN_FWD_SPLIT_WORKERS (>= 1) overrides it.
-int split_workers(int B, int Hkv, int K, int D, int Dv, int rows) {
+// resident at once (four per CU, fewer when the two LDS ring stages of K, V
+// and Q sub-blocks of the kernel that launches need more than 40 KiB),
+// fewer still when even the padded length gives less than kDecodeMinShare
+// sub-blocks each.  ATTN_FWD_SPLIT_WORKERS (>= 1) overrides it.
+int split_workers(int B, int Hkv, int K, int D, int Dv, int rows, const Geometry& geo) {
   if (K <= 0) return 0;
   if (const char* e = std::getenv("ATTN_FWD_SPLIT_WORKERS")) {
     const int v = std::atoi(e);
     if (v >= 1) return v;
   }
-  const int dp = pad_width(D), dvp = pad_width(Dv), qrows = rows <= 16 ? 16 : 32;
+  int dp = pad_width(D), dvp = pad_width(Dv);
+  if (dp > 128 || dvp > 128) dp = dvp = 256;  // the wide decode kernel pads both widths to 256
+  const int qrows = rows <= 16 ? 16 : 32;
   const int stage = kDecodeSub * (dp + dvp) * 2 + qrows * dp * 2;
   const int per_cu = std::min(4, 160 * 1024 / (2 * stage));
-  const int64_t resident = (int64_t)per_cu * 256;
+  const int64_t resident = (int64_t)per_cu * geo.cus;
   const int64_t sub = (int64_t)B * Hkv * ((K + kDecodeSub - 1) / kDecodeSub);
   const int64_t w = (sub + kDecodeMinShare - 1) / kDecodeMinShare;
   return (int)std::max<int64_t>(1, std::min(w, resident));
 }
 
 // Key-range pieces per prefill tile.  The kernel holds two workgroups per CU
-// (512 on the chip); while the tiles alone fill fewer than that, each tile's
-// range is cut so that tiles x pieces reaches about 512, keeping at least
-// kPrefillMinSplitBlocks 64-key blocks per piece so the partial states (the
-// fp32 accumulator of 128 rows, written and read back once: about an eighth
-// of the K/V bytes such a piece streams at D = Dv = 128) and the combine
-// launch stay small next to the piece.  If that leaves some of the 256 CUs
+// (512 on MI355X's 256 CUs); while the tiles alone fill fewer than that, each
+// tile's range is cut so that tiles x pieces reaches about that many, keeping
+// at least kPrefillMinSplitBlocks 64-key blocks per piece so the partial
+// states (the fp32 accumulator of 128 rows, written and read back once: about
+// an eighth of the K/V bytes such a piece streams at D = Dv = 128) and the
+// combine launch stay small next to the piece.  If that leaves some CUs
 // without a workgroup, pieces down to kPrefillMinSplitBlocksIdle blocks are
-// taken to reach 256.  (Measured on MI355X: with 256 workgroups already
+// taken to give every CU one.  (Measured on MI355X: with 256 workgroups already
 // running, 16-block pieces lost to 32-block ones; with 16 running, 16-block
 // pieces won; 8-block pieces never paid for the combine launch.)
 // ATTN_FWD_PREFILL_SPLITS (>= 1) overrides it.
-int prefill_splits(int B, int Hkv, int Q, int group, int K) {
+int prefill_splits(int B, int Hkv, int Q, int group, int K, const Geometry& geo) {
   if (K <= 0) return 1;
   if (const char* e = std::getenv("ATTN_FWD_PREFILL_SPLITS")) {
     const int v = std::atoi(e);
@@ -102,7 +145,7 @@ int prefill_splits(int B, int Hkv, int Q, int group, int K) {
   // The combine pass runs one wave per output row, four to a workgroup.
   if ((int64_t)B * Hkv * group * Q > INT32_MAX) return 1;
   const int64_t tiles = (int64_t)B * Hkv * prefill_group_tiles(Q, group);
-  constexpr int64_t kSlots = 512, kCUs = 256;
+  const int64_t kSlots = 2 * (int64_t)geo.cus, kCUs = geo.cus;
   const int64_t blocks = ((int64_t)K + kPrefillBN - 1) / kPrefillBN;
   int64_t s = 1;
   if (tiles < kSlots) {
@@ -125,7 +168,7 @@ int prefill_split_blocks(int K, int splits) {
 
 // Checks shared by both entry points; fills the plan.
 int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, float scale, bool bf16,
-                   attn_fwd_plan_t* plan) {
+                   const Geometry& geo, attn_fwd_plan_t* plan) {
   (void)window;
   *plan = attn_fwd_plan_t{0, 0, 0, 0};
   if (B < 0 || Hq < 0 || Hkv < 0 || Q < 0 || K < 0 || D < 0 || Dv < 0) return ATTN_ERR_INVALID_ARG;
@@ -144,7 +187,7 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
   const bool narrow = D <= 128 && Dv <= 128, wide = !narrow && D <= 256 && Dv <= 256;
   if (bf16 && Q <= kDecodeMaxQ && ((narrow && group * Q <= kDecodeMaxRows) || (wide && group * Q <= kDecodeMaxRowsWide))) {
     plan->path = 2;
-    plan->split_workers = split_workers(B, Hkv, K, D, Dv, group * Q);
+    plan->split_workers = split_workers(B, Hkv, K, D, Dv, group * Q, geo);
     plan->partial_slots = plan->split_workers > 0 ? B * Hkv + plan->split_workers : 0;
     const int64_t parts = (int64_t)plan->partial_slots * group * Q;
     plan->workspace_bytes = parts * (int64_t)(Dv + 2) * 4;
@@ -159,7 +202,7 @@ int check_and_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int wind
       if (tiles * dv_parts > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
       // Pieces of a fixed number of blocks: the requested count rounded to
       // what whole pieces of ceil(blocks / count) blocks need.
-      const int want = prefill_splits(B, Hkv, Q, group, K);
+      const int want = prefill_splits(B, Hkv, Q, group, K, geo);
       const int blocks = (K + kPrefillBN - 1) / kPrefillBN;
       int ns = want > 1 ? (blocks + prefill_split_blocks(K, want) - 1) / prefill_split_blocks(K, want) : 1;
       if (tiles * ns * dv_parts > (int64_t)INT32_MAX) ns = 1;
@@ -191,7 +234,8 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   if (!causal && window > 0) return ATTN_ERR_INVALID_ARG;
   const bool bf16 = !(flags & ATTN_FWD_FP32);  // a 16-bit type: the MFMA kernels
   attn_fwd_plan_t plan;
-  int st = check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, scale, bf16, &plan);
+  const Geometry geo = device_geometry();
+  int st = check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, scale, bf16, geo, &plan);
   if (st != ATTN_OK || plan.path == 0) return st;
   if (!q || !o || !lse) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * Hkv * K > 0 && (!k || !v)) return ATTN_ERR_INVALID_ARG;
@@ -221,6 +265,7 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
     p.num_pages = paged->num_pages;
   }
 
+  p.n_xcd = geo.xcds;
   p.n_split = 1;
   p.dv_parts = (D > 256 || Dv > 256) ? (Dv + 255) / 256 : 1;
   if (!bf16) return launch_status(launch_fwd_f32(p, stream));
@@ -374,7 +419,7 @@ const char* attn_fwd_strerror(int status) {
 
 int attn_fwd_plan(int B, int Hq, int Hkv, int Q, int K, int D, int Dv, int window, attn_fwd_plan_t* plan) {
   if (!plan) return ATTN_ERR_INVALID_ARG;
-  return attn::check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, 1.0f, true, plan);
+  return attn::check_and_plan(B, Hq, Hkv, Q, K, D, Dv, window, 1.0f, true, attn::device_geometry(), plan);
 }
 
 }  // extern "C"

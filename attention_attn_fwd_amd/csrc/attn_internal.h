@@ -88,6 +88,7 @@ struct Params {
   int n_split;             // prefill: key-range pieces per tile (1: no split)
   int split_blocks;        // prefill: 64-key blocks per piece (piece s starts s * split_blocks into the tile's range)
   int dv_parts;            // prefill, heads over 256: output-channel parts of 256 (1 otherwise)
+  int n_xcd;               // XCDs of the device: workgroup i of a launch runs on XCD i % n_xcd
   // Paged K/V cache (block_table null: contiguous k [B,Hkv,K,D], v [B,Hkv,K,Dv]).
   // Otherwise k [num_pages,Hkv,2^page_shift,D], v [num_pages,Hkv,2^page_shift,Dv]
   // and keys [j << page_shift, (j + 1) << page_shift) of sequence b are in page
@@ -122,6 +123,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t stream);
 
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_prefill_bf16(const Params& p, hipStream_t stream);
+hipError_t launch_prefill_combine(const Params& p, hipStream_t stream);   // merge of a split prefill
 hipError_t launch_decode_bf16(const Params& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, hipStream_t stream);
 
@@ -146,6 +148,7 @@ __host__ __device__ inline int row_delta(int Kb, int Q, int causal_shift) { retu
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
 #define ATTN_LDS __attribute__((address_space(3)))
@@ -313,6 +316,11 @@ struct Elem;
 template <>
 struct Elem<false> {
   __device__ static f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) { return mfma16x16x32(a, b, c); }
+  // v_mfma_f32_32x32x16_bf16: lane l holds A[l%32][8(l/32)+e], B[8(l/32)+e][l%32]
+  // (e = 0..7) and receives C[8(r/4) + 4(l/32) + r%4][l%32] in register r.
+  __device__ static f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
   __device__ static bf16x8 pack(f32x4 lo, f32x4 hi) { return pack_bf16x8(lo, hi); }
   __device__ static uint16_t cvt(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 };
@@ -321,6 +329,10 @@ template <>
 struct Elem<true> {
   __device__ static f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+  }
+  __device__ static f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                    0, 0);
   }
   __device__ static bf16x8 pack(f32x4 lo, f32x4 hi) {

@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "attn_internal.h"
+#include "prefill_common.h"
 
 namespace attn {
 
@@ -88,86 +89,6 @@ struct PrefillShape {
                 "ds_read immediates");
   static_assert(LDS <= 160 * 1024, "LDS of a CU");
 };
-
-// A tile: rows [r0, r0 + 128) of the row list of one (batch, kv-head) group
-// (n_rows rows, row r = query row r % Q of head h_base + r / Q), and the
-// piece `split` of its key range.  `part` numbers (group, split, tile)
-// triples; it indexes the partial states of a split pass.
-struct PrefillTile {
-  int b, kh, h_base, r0, n_rows, split, part, dv_part;
-};
-
-// Tile `rem` of group `grp` (rank order: heaviest causal tile first, heads
-// fastest among per-head tiles).
-__device__ __forceinline__ PrefillTile prefill_tile_of(const Params& p, int grp, int rem) {
-  PrefillTile t;
-  t.b = grp / p.Hkv;
-  t.kh = grp - t.b * p.Hkv;
-  if (prefill_packed(p.Q, p.group)) {
-    t.h_base = t.kh * p.group;
-    t.n_rows = p.group * p.Q;
-    t.r0 = (prefill_group_tiles(p.Q, p.group) - 1 - rem) * kPrefillBM;
-  } else {
-    const int n_qt = (p.Q + kPrefillBM - 1) / kPrefillBM;
-    const int qrank = rem / p.group;
-    t.h_base = t.kh * p.group + (rem - qrank * p.group);
-    t.n_rows = p.Q;
-    t.r0 = (n_qt - 1 - qrank) * kPrefillBM;
-  }
-  t.split = 0;
-  t.part = 0;
-  t.dv_part = 0;
-  return t;
-}
-
-// Block index -> tile.  A virtual group is a (piece, group) pair.  When the
-// virtual groups divide evenly over the 8 XCDs (workgroup i runs on XCD
-// i % 8), each XCD gets whole virtual groups and finishes one (all its
-// tiles, heaviest first, and both output-channel parts of a tile next to
-// each other) before the next, so the workgroups resident on an XCD stream
-// the same K/V through its L2; otherwise the order is heaviest tile first
-// with virtual groups fastest.
-__device__ __forceinline__ PrefillTile prefill_tile(const Params& p) {
-  const int x = blockIdx.x;
-  const int vgroups = p.B * p.Hkv * p.n_split;
-  const int per_grp = prefill_group_tiles(p.Q, p.group);
-  const int per_vg = per_grp * p.dv_parts;  // workgroups per virtual group
-  int vg, remx;
-  if ((vgroups & 7) == 0) {
-    const int xcd = x & 7, slot = x >> 3;
-    const int gi = slot / per_vg;
-    remx = slot - gi * per_vg;
-    vg = gi * 8 + xcd;
-  } else {
-    remx = x / vgroups;
-    vg = x - remx * vgroups;
-  }
-  const int rem = remx / p.dv_parts, dv_part = remx - rem * p.dv_parts;
-  // Split-major: virtual group vg is piece vg / groups of group vg % groups,
-  // so an XCD gets every piece of its groups (pieces late in a range are
-  // often empty; dealing pieces to XCDs would leave the XCDs that got the
-  // first pieces with most of the work).
-  const int groups = p.B * p.Hkv;
-  const int split = vg / groups, grp = vg - split * groups;
-  PrefillTile t = prefill_tile_of(p, grp, rem);
-  t.split = split;
-  t.dv_part = dv_part;
-  t.part = (grp * p.n_split + split) * per_grp + rem;  // a row's pieces lie 128 rows apart
-  return t;
-}
-
-// Query rows r0 .. r1 of a row list (r0 <= r1) lie at positions q + delta with
-// q in [qlo, qhi]: the exact range when the rows belong to one head, else the
-// whole head.
-__device__ __forceinline__ void row_q_range(int r0, int r1, int Q, int* qlo, int* qhi) {
-  if (r0 / Q == r1 / Q) {
-    *qlo = r0 % Q;
-    *qhi = r1 % Q;
-  } else {
-    *qlo = 0;
-    *qhi = Q - 1;
-  }
-}
 
 // EXACT: D == DP and Dv == DVP, so row strides are compile-time constants and
 // no channel is padding (the common case); otherwise padded channels read zero.
@@ -735,6 +656,23 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(Params p) {
   if (lane == 0) p.lse[row] = l > 0.f ? (mx + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// The combine pass of a split prefill: one wave per output row, four rows to a
+// workgroup; CPL channels per lane cover Dv.
+hipError_t launch_prefill_combine(const Params& p, hipStream_t stream) {
+  Params arg = p;
+  void* args[] = {&arg};
+  const dim3 cgrid((unsigned)(((int64_t)p.B * p.Hq * p.Q + 3) / 4));
+  const int cpl = p.Dv <= 128 ? 2 : (p.Dv <= 256 ? 4 : 8);
+  const void* cfn;
+  if (cpl == 2) cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, 2>)
+                            : reinterpret_cast<const void*>(&prefill_combine_kernel<false, 2>);
+  else if (cpl == 4) cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, 4>)
+                                 : reinterpret_cast<const void*>(&prefill_combine_kernel<false, 4>);
+  else cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, 8>)
+                   : reinterpret_cast<const void*>(&prefill_combine_kernel<false, 8>);
+  return hipLaunchKernel(cfn, cgrid, dim3(256), args, 0, stream);
+}
+
 template <int DP, int DVP, int NW, int BN, bool DVSPLIT>
 static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const int64_t tiles = (int64_t)prefill_group_tiles(p.Q, p.group) * p.Hkv * p.B;
@@ -755,11 +693,7 @@ static hipError_t launch_prefill_t(const Params& p, hipStream_t stream) {
   const void* fn = kernels[exact | (p.f16 ? 2 : 0) | (p.block_table ? 4 : 0)];
   hipError_t e = hipLaunchKernel(fn, grid, dim3(64 * NW), args, 0, stream);
   if (e != hipSuccess || p.n_split <= 1) return e;
-  const dim3 cgrid((unsigned)(((int64_t)p.B * p.Hq * p.Q + 3) / 4));  // one wave per output row
-  constexpr int CPL = DVP * (DVSPLIT ? 2 : 1) <= 128 ? 2 : (DVP * (DVSPLIT ? 2 : 1) <= 256 ? 4 : 8);
-  const void* cfn = p.f16 ? reinterpret_cast<const void*>(&prefill_combine_kernel<true, CPL>)
-                          : reinterpret_cast<const void*>(&prefill_combine_kernel<false, CPL>);
-  return hipLaunchKernel(cfn, cgrid, dim3(256), args, 0, stream);
+  return launch_prefill_combine(p, stream);
 }
 
 // Heads up to 128 wide: 4 waves of 32 rows, 64-key blocks.  Up to 256 (padded

@@ -55,7 +55,9 @@
  *   ATTN_FWD_PREFILL_SPLITS=n  key-range pieces per prefill tile (n >= 1,
  *                              at most 32; rounded to whole pieces);
  *   ATTN_FWD_FAIL_ALLOC=1      every scratch allocation fails (the calls
- *                              that need scratch return ATTN_ERR_OOM).
+ *                              that need scratch return ATTN_ERR_OOM);
+ *   ATTN_FWD_CUS=n, ATTN_FWD_XCDS=n  compute units / XCDs the launch plans
+ *                              assume (otherwise queried once per device).
  */
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H

@@ -94,6 +94,36 @@ def test_wide_heads_only_on_the_16bit_path():
     assert af.attn_fwd_plan(64, 64, 8, 1, 32768, 256, 256)["split_workers"] == 512
 
 
+def test_plans_follow_the_device_geometry(monkeypatch):
+    """Worker counts and key-range pieces scale with the compute units the
+    plan assumes (queried once per device; forced here)."""
+    monkeypatch.delenv("ATTN_FWD_SPLIT_WORKERS", raising=False)
+    monkeypatch.delenv("ATTN_FWD_PREFILL_SPLITS", raising=False)
+    decode = (64, 64, 8, 1, 32768, 128, 128)   # batched long-context decode: 4 single-wave workers per CU
+    chunk = (1, 32, 8, 512, 32768, 128, 128)  # 128 prefill tiles over 32768 keys
+    monkeypatch.setenv("ATTN_FWD_CUS", "256")
+    assert af.attn_fwd_plan(*decode)["split_workers"] == 4 * 256
+    assert af.attn_fwd_plan(*chunk)["split_workers"] == 4   # 128 tiles x 4 pieces = 2 per CU
+    monkeypatch.setenv("ATTN_FWD_CUS", "64")
+    assert af.attn_fwd_plan(*decode)["split_workers"] == 4 * 64
+    assert af.attn_fwd_plan(*chunk)["split_workers"] == 1   # the tiles alone fill 2 per CU
+    monkeypatch.setenv("ATTN_FWD_CUS", "304")
+    assert af.attn_fwd_plan(*decode)["split_workers"] == 4 * 304
+    assert af.attn_fwd_plan(*chunk)["split_workers"] == 5   # ceil(608 / 128) pieces
+    # A short problem never gets more workers than it has 4-sub-block shares.
+    assert af.attn_fwd_plan(1, 8, 2, 1, 2053, 80, 96)["split_workers"] == (2 * 65 + 3) // 4
+
+
+def test_wide_decode_ring_sizes_the_worker_count(monkeypatch):
+    """Heads whose widths pad to 64 and 256 run on the kernel padded to 256 on
+    both sides (two 40 KiB ring stages: two workers per CU), not three."""
+    monkeypatch.delenv("ATTN_FWD_SPLIT_WORKERS", raising=False)
+    monkeypatch.setenv("ATTN_FWD_CUS", "256")
+    for D, Dv in [(64, 256), (256, 64), (256, 256), (144, 128)]:
+        assert af.attn_fwd_plan(64, 64, 8, 1, 32768, D, Dv)["split_workers"] == 512, (D, Dv)
+    assert af.attn_fwd_plan(64, 64, 8, 1, 32768, 64, 128)["split_workers"] == 1024
+
+
 @pytest.mark.parametrize("fn", [af.attn_fwd, af.attn_fwd_f32], ids=["bf16", "f32"])
 def test_null_and_misaligned_pointers(fn):
     fake = 1 << 20

@@ -1,8 +1,10 @@
 """The five benchmark workloads at full size, in the launch configuration the
-bench times.  The two small ones are compared against the oracle in full; the
-three large ones on sampled rows (the oracle computes rows one by one), plus
-whole-output properties that hold at any size: every row written, no NaN/Inf,
-LSE = -inf exactly on the rows without a legal key, bitwise-identical reruns.
+bench times, compared with the fp64 oracle on every element: the two small
+ones in one piece, the three large ones one sequence at a time (each
+sequence of a batch is its own problem, so the oracle runs on the slice),
+after one GPU run per configuration.  Whole-output properties are checked
+as well: every row written, no NaN/Inf, LSE = -inf exactly on the rows
+without a legal key, bitwise-identical reruns, inputs unchanged.
 """
 import numpy as np
 import pytest
@@ -36,43 +38,73 @@ def _empty_rows_mask(w):
     return np.broadcast_to(q + kb - w.Q < 0, (w.B, w.Hq, w.Q))
 
 
-def _run_config(idx, orc, n_rows):
+def _gpu_config(idx):
+    """One GPU run of configuration idx with the whole-output checks; returns the
+    workload, its host inputs and the GPU outputs (float64 host arrays)."""
     w = inputs.config(idx)
     say(f"[config {idx}] {w.name} {w.shape_tuple} {w.dtype} W={w.window}")
     q = w.gen_q()
     k = w.gen_k(padding="zero")
     v = w.gen_v(padding="zero")
-    o, lse = run_gpu(w, q, k, v, check_inputs=(idx <= 3))
+    o, lse = run_gpu(w, q, k, v, check_inputs=(idx <= 4))
     empty = _empty_rows_mask(w)
     assert np.array_equal(np.isneginf(lse), empty), "LSE -inf pattern differs from the rows without keys"
     assert np.all(o[empty] == 0.0)
     assert np.isfinite(o).all() and not np.isnan(lse).any()
-    if n_rows is None:
-        ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
-        return compare(o, lse, ro, rl, w.dtype, w.name)
-    rows = _sample_rows(w, n_rows)
-    ro, rl = orc.rows(q, k, v, rows, seqlens=w.seqlens, window=w.window, scale=w.scale)
-    return compare(o.reshape(-1, w.Dv)[rows], lse.reshape(-1)[rows], ro, rl, w.dtype, f"{w.name} ({len(rows)} rows)")
+    return w, q, k, v, o, lse
+
+
+def _compare_sequence(run, orc, b):
+    """Every element of sequence b against the oracle run on that sequence alone."""
+    w, q, k, v, o, lse = run
+    sl = None if w.seqlens is None else w.seqlens[b:b + 1]
+    say(f"[config] {w.name} sequence {b} (K_b = {w.kb(b)}): full oracle")
+    ro, rl = orc.fwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], seqlens=sl, window=w.window, scale=w.scale)
+    return compare(o[b:b + 1], lse[b:b + 1], ro, rl, w.dtype, f"{w.name} sequence {b}")
+
+
+@pytest.fixture(scope="module")
+def run3():
+    return _gpu_config(3)
+
+
+@pytest.fixture(scope="module")
+def run4():
+    return _gpu_config(4)
+
+
+@pytest.fixture(scope="module")
+def run5():
+    return _gpu_config(5)
 
 
 def test_config1_tiny_fp32(orc):
-    _run_config(1, orc, None)
+    w, q, k, v, o, lse = _gpu_config(1)
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
+    compare(o, lse, ro, rl, w.dtype, w.name)
 
 
 def test_config2_decode_tail(orc):
-    _run_config(2, orc, None)
+    w, q, k, v, o, lse = _gpu_config(2)
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
+    compare(o, lse, ro, rl, w.dtype, w.name)
 
 
-def test_config3_dense_prefill(orc):
-    _run_config(3, orc, 384)
+@pytest.mark.parametrize("b", range(4))
+def test_config3_dense_prefill_full(orc, run3, b):
+    _compare_sequence(run3, orc, b)
 
 
-def test_config4_varlen_window(orc):
-    _run_config(4, orc, 384)
+@pytest.mark.parametrize("b", range(16))
+def test_config4_varlen_window_full(orc, run4, b):
+    _compare_sequence(run4, orc, b)
 
 
-def test_config5_long_decode(orc):
-    _run_config(5, orc, 768)
+def test_config5_long_decode_full(orc, run5):
+    w, q, k, v, o, lse = run5
+    say(f"[config] {w.name}: full oracle over all {w.B} sequences")
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
+    compare(o, lse, ro, rl, w.dtype, w.name)
 
 
 # The option workloads the bench times beside the step, at their full sizes,

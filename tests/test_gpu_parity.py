@@ -135,6 +135,36 @@ def test_prefill_forced_splits(orc, shape, splits, monkeypatch):
     _check(w, orc=orc, tag=f" splits={splits}")
 
 
+# The XCD-aware tile order only changes which workgroup computes a tile: any
+# assumed XCD count (1 = plain heaviest-first order) gives bitwise the same
+# output, with and without split key ranges; and a plan for fewer CUs than
+# the device has (more pieces per tile, fewer workers) stays correct.
+@pytest.mark.parametrize("shape,splits", [((2, 8, 2, 300, 700, 128, 128), 1), ((1, 16, 4, 200, 2000, 64, 128), 3),
+                                          ((1, 8, 1, 100, 4100, 256, 256), 1)], ids=["plain", "split", "wide"])
+def test_xcd_order_is_bitwise_neutral(orc, shape, splits, monkeypatch):
+    if splits > 1:
+        monkeypatch.setenv("ATTN_FWD_PREFILL_SPLITS", str(splits))
+    w = inputs.Workload("xcd", *shape, seqlens=np.array([shape[4], shape[4] // 2][:shape[0]], np.int32))
+    q, k, v = w.gen_q(), w.gen_k(), w.gen_v()
+    res = []
+    for xcds in ("1", "8", "3"):
+        monkeypatch.setenv("ATTN_FWD_XCDS", xcds)
+        say(f"[case] xcd order {w.shape_tuple} xcds={xcds} splits={splits}")
+        res.append(run_gpu(w, q, k, v, repeat_bitwise=False))
+    for o, lse in res[1:]:
+        assert np.array_equal(o, res[0][0]) and np.array_equal(np.nan_to_num(lse), np.nan_to_num(res[0][1]))
+    ro, rl = orc.fwd(q, k, v, seqlens=w.seqlens, window=w.window, scale=w.scale)
+    compare(res[0][0], res[0][1], ro, rl, w.dtype, "xcd order")
+
+
+def test_small_chip_plan_is_correct(orc, monkeypatch):
+    """Plans for a 40-CU chip: more decode shares per worker and more prefill pieces."""
+    monkeypatch.setenv("ATTN_FWD_CUS", "40")
+    for shape in [(4, 16, 4, 1, 5000, 128, 128), (1, 8, 2, 200, 6000, 128, 128)]:
+        w = inputs.Workload("small_chip", *shape, seqlens=np.linspace(0, shape[4], shape[0]).astype(np.int32))
+        _check(w, orc=orc, tag=" cus=40")
+
+
 # Heads wider than 128 (up to 256): the 8-wave prefill form (decode shapes
 # of more than 16 packed rows included: split key ranges) and the split-KV
 # decode kernel up to 16 rows; padded widths (D or Dv below 256), D != Dv,

@@ -28,18 +28,32 @@ def test_oracle_rejects_bad_sizes(orc):
         orc.fwd(q, k, k, seqlens=np.array([6], np.int32))  # length beyond K
 
 
-def test_oracle_rows_match_full(orc):
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("mode", ["causal_window", "causal", "noncausal", "noncausal_empty"])
+def test_oracle_rows_match_full(orc, dtype, mode):
+    """The row-sampled oracle (used on the large workloads) is the full oracle's
+    arithmetic row by row: bitwise the same rows, in every storage type and in
+    both masking modes, with per-sequence lengths (one sequence empty in the
+    last mode)."""
+    from attention_attn_fwd_amd import inputs
     rng = np.random.default_rng(5)
-    B, Hq, Hkv, Q, K, D, Dv = 2, 4, 2, 7, 19, 16, 8
-    q = rng.standard_normal((B, Hq, Q, D)).astype(np.float32)
-    k = rng.standard_normal((B, Hkv, K, D)).astype(np.float32)
-    v = rng.standard_normal((B, Hkv, K, Dv)).astype(np.float32)
-    sl = np.array([19, 4], np.int32)
-    o, lse = orc.fwd(q, k, v, seqlens=sl, window=5)
-    rows = np.array([0, 5, 13, 27, 55], np.int64)
-    ro, rl = orc.rows(q, k, v, rows, seqlens=sl, window=5)
+    B, Hq, Hkv, Q, K, D, Dv = 3, 4, 2, 7, 19, 16, 8
+    qf = rng.standard_normal((B, Hq, Q, D)).astype(np.float32)
+    kf = rng.standard_normal((B, Hkv, K, D)).astype(np.float32)
+    vf = rng.standard_normal((B, Hkv, K, Dv)).astype(np.float32)
+    conv = {"f32": lambda a: a, "f16": lambda a: a.astype(np.float16), "bf16": inputs.f32_to_bf16_bits}[dtype]
+    q, k, v = conv(qf), conv(kf), conv(vf)
+    sl = np.array([19, 4, 0 if mode == "noncausal_empty" else 11], np.int32)
+    kw = {"causal_window": dict(seqlens=sl, window=5), "causal": dict(seqlens=sl),
+          "noncausal": dict(seqlens=sl, causal=False), "noncausal_empty": dict(seqlens=sl, causal=False)}[mode]
+    o, lse = orc.fwd(q, k, v, **kw)
+    rows = np.arange(B * Hq * Q, dtype=np.int64)[::3]
+    ro, rl = orc.rows(q, k, v, rows, **kw)
     np.testing.assert_array_equal(ro, o.reshape(-1, Dv)[rows])
     np.testing.assert_array_equal(rl, lse.reshape(-1)[rows])
+    if mode == "noncausal_empty":  # the empty sequence's rows: O = 0, LSE = -inf
+        sel = rows // (Hq * Q) == 2
+        assert np.all(ro[sel] == 0.0) and np.all(np.isneginf(rl[sel]))
 
 
 def test_oracle_bf16_inputs(orc):
