@@ -15,14 +15,14 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
 
-ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_OOM, ATTN_ERR_HIP = range(5)
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_OOM, ATTN_ERR_HIP, ATTN_ERR_SCRATCH_LIMIT = range(6)
 PATH_NONE, PATH_PREFILL, PATH_DECODE = 0, 1, 2
 # attn_fwd_ex flags
 ATTN_FWD_FP16, ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL = 1, 2, 4
 
 # Every function the header declares; a CPU test checks the library exports all of them.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_paged", "attn_bwd", "attn_fwd_strerror",
-           "attn_fwd_plan")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_paged", "attn_bwd",
+           "attn_fwd_strerror", "attn_fwd_plan")
 
 
 class AttnError(RuntimeError):
@@ -65,6 +65,8 @@ def load():
         lib.attn_fwd_f32.restype = ci
         lib.attn_fwd_ex.argtypes = sig[:-1] + [ci, vp]
         lib.attn_fwd_ex.restype = ci
+        lib.attn_fwd_noalloc.argtypes = sig[:-1] + [ci, vp]
+        lib.attn_fwd_noalloc.restype = ci
         lib.attn_fwd_paged.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, vp, ci, ci, ci, vp, ci, cf, ci, vp]
         lib.attn_fwd_paged.restype = ci
         lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, ci, cf, ci, vp]
@@ -116,6 +118,12 @@ def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, sca
     """Raw C call with option flags (ATTN_FWD_FP16 / _FP32 / _NONCAUSAL); returns the status."""
     return load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
                               _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
+
+
+def attn_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, flags, stream) -> int:
+    """Raw C call of the entry point that allocates nothing (library-held scratch); returns the status."""
+    return load().attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Q, K, D, Dv,
+                                   _ptr(seqlens_k), int(window), float(scale), int(flags), _stream(stream))
 
 
 def attn_fwd_paged(q, k_pages, v_pages, o, lse, B, Hq, Hkv, Q, D, Dv, block_table, pages_per_seq, page_size,

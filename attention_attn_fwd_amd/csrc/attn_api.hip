@@ -12,6 +12,14 @@
 #include "../../include/attn_fwd.h"
 #include "attn_internal.h"
 
+// Scratch of attn_fwd_noalloc (the split-KV partial states): device memory
+// that exists on every GPU the library runs on for the life of the process.
+// In host code this name is only a stand-in for the symbol; the device
+// address is looked up once per device (noalloc_scratch below) and only that
+// address is ever passed to a kernel.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
 namespace attn {
 namespace {
 
@@ -44,6 +52,29 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   });
   *out = dp.pool;
   return dp.err;
+}
+
+// Device address of `scratch` on each device, looked up on the first
+// attn_fwd_noalloc call on that device, with that device current.
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& ss = g_scratch[dev];
+  std::call_once(ss.once, [&]() {
+    ss.err = hipGetSymbolAddress(&ss.ptr, HIP_SYMBOL(scratch));
+    if (ss.err == hipSuccess && !ss.ptr) ss.err = hipErrorInvalidSymbol;
+  });
+  *out = ss.ptr;
+  return ss.err;
 }
 
 // Chip geometry, queried once per device: compute units and XCDs (the
@@ -223,10 +254,12 @@ struct PagedArgs {
 };
 
 // flags: ATTN_FWD_FP16 / ATTN_FWD_FP32 select the element type (bf16 when
-// neither), ATTN_FWD_NONCAUSAL drops the causal limit.
+// neither), ATTN_FWD_NONCAUSAL drops the causal limit.  noalloc: the split-KV
+// scratch is the library's static `scratch` (no allocation; a plan that
+// needs more returns ATTN_ERR_SCRATCH_LIMIT before anything is launched).
 int run(int flags, const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
         int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, void* stream_,
-        const PagedArgs* paged = nullptr) {
+        const PagedArgs* paged = nullptr, bool noalloc = false) {
   constexpr int kKnown = ATTN_FWD_FP16 | ATTN_FWD_FP32 | ATTN_FWD_NONCAUSAL;
   if ((flags & ~kKnown) != 0) return ATTN_ERR_INVALID_ARG;
   if ((flags & ATTN_FWD_FP16) && (flags & ATTN_FWD_FP32)) return ATTN_ERR_INVALID_ARG;
@@ -281,23 +314,33 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
     p.n_workers = plan.split_workers;
     parts = (int64_t)plan.partial_slots * p.rows;
   }
-  const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
-  if (fail && fail[0] == '1') return ATTN_ERR_OOM;
   void* ws = nullptr;
-  if (parts > 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-    hipMemPool_t pool = nullptr;
-    if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
-    if (hipMallocFromPoolAsync(&ws, (size_t)plan.workspace_bytes, pool, stream) != hipSuccess || !ws)
-      return ATTN_ERR_OOM;
+  if (noalloc) {
+    // Every partial slot the kernels read is written in the same call (a piece
+    // with no key writes m = -inf), so the scratch needs no clearing.
+    if (plan.workspace_bytes > kNoAllocScratchBytes) return ATTN_ERR_SCRATCH_LIMIT;
+    if (parts > 0 && noalloc_scratch(&ws) != hipSuccess) {
+      (void)hipGetLastError();
+      return ATTN_ERR_HIP;
+    }
+  } else {
+    const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
+    if (fail && fail[0] == '1') return ATTN_ERR_OOM;
+    if (parts > 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+      hipMemPool_t pool = nullptr;
+      if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
+      if (hipMallocFromPoolAsync(&ws, (size_t)plan.workspace_bytes, pool, stream) != hipSuccess || !ws)
+        return ATTN_ERR_OOM;
+    }
   }
   float* wsf = static_cast<float*>(ws);
   p.ws_acc = wsf;  // [parts][Dv] first: 16-byte aligned rows
   p.ws_m = wsf + parts * Dv;
   p.ws_l = p.ws_m + parts;
   const int launched = launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
-  if (ws) {
+  if (ws && !noalloc) {
     const hipError_t ef = hipFreeAsync(ws, stream);
     if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;
   }
@@ -322,6 +365,12 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream) {
   return attn::run(flags, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream);
+}
+
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Q, int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags,
+                     void* stream) {
+  return attn::run(flags, q, k, v, o, lse, B, Hq, Hkv, Q, K, D, Dv, seqlens_k, window, scale, stream, nullptr, true);
 }
 
 int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse, int B, int Hq,
@@ -413,6 +462,8 @@ const char* attn_fwd_strerror(int status) {
       return "unsupported size (D and Dv must be multiples of 16 in [16, 512], [16, 128] in fp32)";
     case ATTN_ERR_OOM: return "scratch allocation failed";
     case ATTN_ERR_HIP: return "HIP launch or runtime error";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "the call needs more split-KV scratch than attn_fwd_noalloc holds (64 MiB); use attn_fwd_ex";
     default: return "unknown status";
   }
 }

@@ -73,7 +73,8 @@ enum attn_status {
   ATTN_ERR_INVALID_ARG = 1, /* nothing launched */
   ATTN_ERR_UNSUPPORTED = 2, /* nothing launched */
   ATTN_ERR_OOM = 3,         /* scratch allocation failed; nothing launched */
-  ATTN_ERR_HIP = 4          /* a HIP call or launch failed */
+  ATTN_ERR_HIP = 4,         /* a HIP call or launch failed */
+  ATTN_ERR_SCRATCH_LIMIT = 5 /* attn_fwd_noalloc: more scratch than it holds; nothing launched */
 };
 
 /*
@@ -123,6 +124,25 @@ enum attn_fwd_flags { ATTN_FWD_FP16 = 1, ATTN_FWD_FP32 = 2, ATTN_FWD_NONCAUSAL =
 
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Q,
                 int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags, void* stream);
+
+/*
+ * attn_fwd_ex for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, kernels, launch plan and results (bitwise those of
+ * attn_fwd_ex), but the scratch of the split-KV passes is a 64 MiB array
+ * held by the library on every GPU it runs on until the process ends, so
+ * the call allocates and frees nothing.  The caller still passes every
+ * input and output.  A plan whose scratch (attn_fwd_plan's workspace_bytes)
+ * exceeds 64 MiB returns ATTN_ERR_SCRATCH_LIMIT with nothing launched; every
+ * other status is as for attn_fwd_ex.  The first call on a device looks up
+ * that device's copy of the array.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams, or queued
+ * ahead of one another's completion on different streams) race; calls on
+ * one stream are ordered and safe.
+ */
+int attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                     int Q, int K, int D, int Dv, const int32_t* seqlens_k, int window, float scale, int flags,
+                     void* stream);
 
 /*
  * Paged K/V cache (block-table indirection, as a serving engine keeps it;
