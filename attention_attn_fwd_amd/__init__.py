@@ -9,5 +9,5 @@ from ._binding import (  # noqa: F401
     ATTN_ERR_HIP, ATTN_ERR_INVALID_ARG, ATTN_ERR_OOM, ATTN_ERR_SCRATCH_LIMIT, ATTN_ERR_UNSUPPORTED, ATTN_FWD_FP16,
     ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL, ATTN_OK, EXPORTS, LIB_PATH, PATH_DECODE, PATH_NONE, PATH_PREFILL, AttnError,
     attn_bwd, attn_fwd, attn_fwd_ex, attn_fwd_f32, attn_fwd_noalloc, attn_fwd_paged, attn_fwd_plan,
-    attn_fwd_strerror, backward, forward, forward_paged, load, strerror,
+    attn_fwd_release_scratch, attn_fwd_strerror, backward, forward, forward_paged, load, strerror,
 )

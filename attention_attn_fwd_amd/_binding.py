@@ -22,7 +22,7 @@ ATTN_FWD_FP16, ATTN_FWD_FP32, ATTN_FWD_NONCAUSAL = 1, 2, 4
 
 # Every function the header declares; a CPU test checks the library exports all of them.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_fwd_noalloc", "attn_fwd_paged", "attn_bwd",
-           "attn_fwd_strerror", "attn_fwd_plan")
+           "attn_fwd_strerror", "attn_fwd_plan", "attn_fwd_release_scratch")
 
 
 class AttnError(RuntimeError):
@@ -75,6 +75,8 @@ def load():
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_plan.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, ctypes.POINTER(_Plan)]
         lib.attn_fwd_plan.restype = ci
+        lib.attn_fwd_release_scratch.argtypes = []
+        lib.attn_fwd_release_scratch.restype = ci
         _lib = lib
     return _lib
 
@@ -140,6 +142,11 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Q, K, D, Dv, seqlens
     return load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                            B, Hq, Hkv, Q, K, D, Dv, _ptr(seqlens_k), int(window), float(scale), int(flags),
                            _stream(stream))
+
+
+def attn_fwd_release_scratch() -> int:
+    """Free the library's per-stream scratch buffers (waits for each device first); returns the status."""
+    return load().attn_fwd_release_scratch()
 
 
 def attn_fwd_plan(B, Hq, Hkv, Q, K, D, Dv, window=0) -> dict:

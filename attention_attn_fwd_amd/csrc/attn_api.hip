@@ -1,5 +1,5 @@
 // C ABI of libattn_fwd.so (declared in include/attn_fwd.h): argument checks,
-// launch planning, stream-ordered scratch for the split-KV path, launches.
+// launch planning, per-stream scratch for the split-KV path, launches.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
+#include <vector>
 
 #include "../../include/attn_fwd.h"
 #include "attn_internal.h"
@@ -25,33 +26,74 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-// One private stream-ordered pool per device.  Its release threshold is
-// unbounded, so scratch freed at the end of a call is reused by the next call
-// on the same device instead of going back to the driver at each sync.
-struct DevicePool {
-  std::once_flag once;
-  hipMemPool_t pool = nullptr;
-  hipError_t err = hipSuccess;
+// Scratch of the allocating entry points: one device buffer per (device,
+// stream) the library has been called on, grown when a call needs more and
+// kept for the next call.  Calls on one stream run in stream order, so two
+// calls never use one buffer at once; calls on different streams get
+// different buffers.  Growing first waits for the stream (its earlier calls
+// may still read the old buffer), then frees and reallocates: rare, and the
+// only host synchronisation these calls make.  (A stream-ordered pool
+// allocation and free per call made every call wait on the host for the
+// stream's earlier work, so no call could be queued ahead of the GPU.)
+struct StreamScratch {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
 };
-DevicePool g_pools[kMaxDevices];
+std::mutex g_ws_mutex;
+std::vector<StreamScratch> g_ws;
 
-hipError_t device_pool(int dev, hipMemPool_t* out) {
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  DevicePool& dp = g_pools[dev];
-  std::call_once(dp.once, [&]() {
-    hipMemPoolProps props = {};
-    props.allocType = hipMemAllocationTypePinned;
-    props.handleTypes = hipMemHandleTypeNone;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    dp.err = hipMemPoolCreate(&dp.pool, &props);
-    if (dp.err == hipSuccess) {
-      uint64_t threshold = UINT64_MAX;
-      dp.err = hipMemPoolSetAttribute(dp.pool, hipMemPoolAttrReleaseThreshold, &threshold);
-    }
-  });
-  *out = dp.pool;
-  return dp.err;
+int stream_scratch(hipStream_t stream, size_t bytes, void** out) {
+  const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
+  if (fail && fail[0] == '1') return ATTN_ERR_OOM;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  StreamScratch* e = nullptr;
+  for (StreamScratch& s : g_ws)
+    if (s.dev == dev && s.stream == stream) e = &s;
+  if (e && e->bytes >= bytes) {
+    *out = e->ptr;
+    return ATTN_OK;
+  }
+  size_t want = bytes;
+  if (e) {
+    want = std::max(want, e->bytes + e->bytes / 2);
+    if (hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
+    if (hipFree(e->ptr) != hipSuccess) return ATTN_ERR_HIP;
+    e->ptr = nullptr;
+    e->bytes = 0;
+  }
+  constexpr size_t kGrain = (size_t)2 << 20;
+  want = (want + kGrain - 1) / kGrain * kGrain;
+  void* ptr = nullptr;
+  if (hipMalloc(&ptr, want) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return ATTN_ERR_OOM;
+  }
+  if (e) {
+    e->ptr = ptr;
+    e->bytes = want;
+  } else {
+    g_ws.push_back(StreamScratch{dev, stream, ptr, want});
+  }
+  *out = ptr;
+  return ATTN_OK;
+}
+
+int release_stream_scratch() {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+  int status = ATTN_OK;
+  for (StreamScratch& s : g_ws) {
+    if (hipSetDevice(s.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(s.ptr) != hipSuccess)
+      status = ATTN_ERR_HIP;
+  }
+  g_ws.clear();
+  if (hipSetDevice(cur) != hipSuccess) status = ATTN_ERR_HIP;
+  return status;
 }
 
 // Device address of `scratch` on each device, looked up on the first
@@ -304,7 +346,8 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
   if (!bf16) return launch_status(launch_fwd_f32(p, stream));
   if (plan.path == 1 && plan.split_workers <= 1) return launch_status(launch_prefill_bf16(p, stream));
 
-  // Split-KV decode or prefill: scratch from the device's stream-ordered pool.
+  // Split-KV decode or prefill: partial states in scratch (the stream's buffer,
+  // or the library-held array for attn_fwd_noalloc).
   int64_t parts;
   if (plan.path == 1) {
     p.n_split = plan.split_workers;
@@ -323,28 +366,15 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
       (void)hipGetLastError();
       return ATTN_ERR_HIP;
     }
-  } else {
-    const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
-    if (fail && fail[0] == '1') return ATTN_ERR_OOM;
-    if (parts > 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-      hipMemPool_t pool = nullptr;
-      if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
-      if (hipMallocFromPoolAsync(&ws, (size_t)plan.workspace_bytes, pool, stream) != hipSuccess || !ws)
-        return ATTN_ERR_OOM;
-    }
+  } else if (parts > 0) {
+    const int sst = stream_scratch(stream, (size_t)plan.workspace_bytes, &ws);
+    if (sst != ATTN_OK) return sst;
   }
   float* wsf = static_cast<float*>(ws);
   p.ws_acc = wsf;  // [parts][Dv] first: 16-byte aligned rows
   p.ws_m = wsf + parts * Dv;
   p.ws_l = p.ws_m + parts;
-  const int launched = launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
-  if (ws && !noalloc) {
-    const hipError_t ef = hipFreeAsync(ws, stream);
-    if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;
-  }
-  return launched;
+  return launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
 }
 
 }  // namespace
@@ -434,25 +464,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   p.abs_scale = std::fabs(scale);
 
   // Scratch: delta and lse2 per row.
-  const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
-  if (fail && fail[0] == '1') return ATTN_ERR_OOM;
   void* ws = nullptr;
   if (rows > 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-    hipMemPool_t pool = nullptr;
-    if (device_pool(dev, &pool) != hipSuccess) return ATTN_ERR_HIP;
-    if (hipMallocFromPoolAsync(&ws, (size_t)(rows * 2 * 4), pool, stream) != hipSuccess || !ws) return ATTN_ERR_OOM;
+    const int sst = stream_scratch(stream, (size_t)(rows * 2 * 4), &ws);
+    if (sst != ATTN_OK) return sst;
   }
   p.delta = static_cast<float*>(ws);
   p.lse2 = p.delta ? p.delta + rows : nullptr;
-  const int launched = launch_status(launch_bwd_bf16(p, stream));
-  if (ws) {
-    const hipError_t ef = hipFreeAsync(ws, stream);
-    if (launched == ATTN_OK && ef != hipSuccess) return ATTN_ERR_HIP;
-  }
-  return launched;
+  return launch_status(launch_bwd_bf16(p, stream));
 }
+
+int attn_fwd_release_scratch(void) { return attn::release_stream_scratch(); }
 
 const char* attn_fwd_strerror(int status) {
   switch (status) {

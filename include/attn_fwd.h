@@ -28,13 +28,21 @@
  * return after enqueueing kernels on `stream`, with no host synchronisation;
  * a device fault surfaces at the caller's next synchronisation.
  *
- * Ownership: the caller owns every buffer.  The library keeps no pointer past
- * the call's stream-ordered completion and frees nothing it did not
- * allocate.  Inputs are only read.  o and lse must not alias the inputs.
- * Scratch for the split-KV passes (decode, and prefill when its tiles are
- * few) comes from a library-owned, stream-ordered HIP memory pool
- * (allocated and released on `stream`), so concurrent calls on different
- * streams do not share scratch.
+ * Ownership: the caller owns every buffer.  The library keeps no pointer to
+ * a caller's buffer past the call's stream-ordered completion and frees
+ * nothing it did not allocate.  Inputs are only read.  o and lse must not
+ * alias the inputs.  Scratch for the split-KV passes (decode, and prefill
+ * when its tiles are few) and for the backward is a library-owned device
+ * buffer per (device, stream) the library has been called on: calls on one
+ * stream run in stream order and share it, calls on different streams never
+ * do.  A call that needs more than the stream's buffer holds waits for the
+ * stream, then frees and reallocates it (at least 1.5x, rounded to 2 MiB);
+ * no other call synchronises with the host, so calls can be queued ahead of
+ * the GPU.  The buffers are kept until attn_fwd_release_scratch or process
+ * exit.  The buffer is keyed by the stream handle: before a stream is
+ * destroyed, its calls must have completed (as for any work on it).  Under
+ * HIP graph capture, make one call of the same or larger size on the stream
+ * first (a capture cannot wait for the stream), or use attn_fwd_noalloc.
  *
  * Head widths: D and Dv up to 128 run on kernels sized for them; wider
  * heads run on 8-wave forms of the prefill kernel (decode with more than 16
@@ -179,8 +187,8 @@ int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void
  * storage type (bf16, or IEEE binary16 with ATTN_FWD_FP16); every element is
  * written, keys at or past K_b get 0.  Sums are fp32; the weights and dS are
  * rounded to the storage type for the matrix products.  Deterministic (no
- * atomics).  Scratch (two floats per query row) comes from the same
- * stream-ordered pool as the forward's.
+ * atomics).  Scratch (two floats per query row) is the stream's buffer, as
+ * for the forward.
  *
  * Returns as attn_fwd_ex, and ATTN_ERR_UNSUPPORTED for ATTN_FWD_FP32 or D, Dv
  * outside multiples of 16 in [16, 256] (above 128, dK and dV are computed by
@@ -189,6 +197,17 @@ int attn_fwd_paged(const void* q, const void* k_pages, const void* v_pages, void
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
              void* dk, void* dv, int B, int Hq, int Hkv, int Q, int K, int D, int Dv, const int32_t* seqlens_k,
              int window, float scale, int flags, void* stream);
+
+/*
+ * Frees every scratch buffer the allocating entry points hold (one per
+ * device and stream they were called on), after waiting for each of those
+ * devices to finish its work.  Calls made afterwards allocate again.  Not
+ * to be called while another host thread is inside a call of this library.
+ * Returns ATTN_OK, or ATTN_ERR_HIP if a wait or free failed (the buffers
+ * are forgotten either way).  This is the library's own memory management;
+ * it computes nothing, so no passage of the attention write-ups defines it.
+ */
+int attn_fwd_release_scratch(void);
 
 /* Static description of a status code; never NULL. */
 const char* attn_fwd_strerror(int status);
@@ -201,7 +220,7 @@ const char* attn_fwd_strerror(int status);
  * into split_workers equal contiguous shares (0 when K == 0), each giving
  * one partial softmax state per group piece; partial_slots bounds the
  * pieces (B*Hkv + split_workers) and workspace_bytes is the scratch the
- * decode path takes from the pool for them (partial_slots * g*Q rows *
+ * decode path needs for them (partial_slots * g*Q rows *
  * (Dv + 2) floats).  On the prefill path split_workers is the number of
  * pieces each 128-row tile's key range is cut into (1: none; more when the
  * tiles alone would leave most of the GPU idle), partial_slots the
