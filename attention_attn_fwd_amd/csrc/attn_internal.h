@@ -58,8 +58,8 @@ constexpr int kDecodeMaxRowsWide = 16;
 // Each worker of the split pass takes at least kDecodeMinShare sub-blocks.
 constexpr int kDecodeMinShare = 4;
 
-// fp32 path: one workgroup of 256 threads per (batch, head, 32 query rows).
-constexpr int kF32Rows = 32;
+// fp32 path: one workgroup of 256 threads per (batch, head, 16 query rows).
+constexpr int kF32Rows = 16;
 constexpr int kF32Keys = 32;
 
 struct Params {
