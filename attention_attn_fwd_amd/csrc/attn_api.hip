@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -28,58 +29,97 @@ constexpr int kMaxDevices = 64;
 
 // Scratch of the allocating entry points: one device buffer per (device,
 // stream) the library has been called on, grown when a call needs more and
-// kept for the next call.  Calls on one stream run in stream order, so two
-// calls never use one buffer at once; calls on different streams get
-// different buffers.  Growing first waits for the stream (its earlier calls
-// may still read the old buffer), then frees and reallocates: rare, and the
-// only host synchronisation these calls make.  (A stream-ordered pool
-// allocation and free per call made every call wait on the host for the
-// stream's earlier work, so no call could be queued ahead of the GPU.)
+// kept for the next call; calls on different streams get different buffers.
+// Each buffer carries an event recorded after the kernels of the last call
+// that used it, and a call first makes its stream wait for that event: on
+// the same stream the wait is already implied by stream order, and when a
+// destroyed stream's handle comes back as a new stream, the new stream's
+// call cannot start before the old stream's last call has finished with the
+// buffer.  Growing waits on the host for that event, then frees and
+// reallocates: rare, and the only host synchronisation these calls make.
+// (A stream-ordered pool allocation and free per call made every call wait
+// on the host for the stream's earlier work, so no call could be queued
+// ahead of the GPU.)  One mutex covers a call from the lookup to the event
+// record, so a buffer cannot be regrown while another host thread's call
+// that uses it is being enqueued.  Under graph capture the buffer is used as
+// it stands (no event operations, which a capture cannot take across its
+// boundary); a capture that would need a larger buffer fails.
 struct StreamScratch {
   int dev;
   hipStream_t stream;
   void* ptr;
   size_t bytes;
+  hipEvent_t last_use;  // null until the first call records it
 };
 std::mutex g_ws_mutex;
-std::vector<StreamScratch> g_ws;
+std::vector<std::unique_ptr<StreamScratch>> g_ws;
 
-int stream_scratch(hipStream_t stream, size_t bytes, void** out) {
+// Holds the scratch mutex for one call from acquire() on; after the
+// launches, record() marks the buffer's last use on the call's stream.
+class ScratchCall {
+ public:
+  ScratchCall() : lock_(g_ws_mutex, std::defer_lock) {}
+  // The stream's buffer of at least `bytes` bytes, with `stream` ordered
+  // after the buffer's last use.
+  int acquire(hipStream_t stream, size_t bytes, void** out);
+  int record();
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  StreamScratch* slot_ = nullptr;
+  hipStream_t stream_ = nullptr;
+  bool capturing_ = false;
+};
+
+int ScratchCall::acquire(hipStream_t stream, size_t bytes, void** out) {
   const char* fail = std::getenv("ATTN_FWD_FAIL_ALLOC");
   if (fail && fail[0] == '1') return ATTN_ERR_OOM;
+  lock_.lock();
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return ATTN_ERR_HIP;
+  capturing_ = cap != hipStreamCaptureStatusNone;
   StreamScratch* e = nullptr;
-  for (StreamScratch& s : g_ws)
-    if (s.dev == dev && s.stream == stream) e = &s;
-  if (e && e->bytes >= bytes) {
-    *out = e->ptr;
-    return ATTN_OK;
-  }
-  size_t want = bytes;
-  if (e) {
-    want = std::max(want, e->bytes + e->bytes / 2);
-    if (hipStreamSynchronize(stream) != hipSuccess) return ATTN_ERR_HIP;
-    if (hipFree(e->ptr) != hipSuccess) return ATTN_ERR_HIP;
-    e->ptr = nullptr;
-    e->bytes = 0;
-  }
-  constexpr size_t kGrain = (size_t)2 << 20;
-  want = (want + kGrain - 1) / kGrain * kGrain;
-  void* ptr = nullptr;
-  if (hipMalloc(&ptr, want) != hipSuccess || !ptr) {
-    (void)hipGetLastError();
-    return ATTN_ERR_OOM;
-  }
-  if (e) {
+  for (auto& s : g_ws)
+    if (s->dev == dev && s->stream == stream) e = s.get();
+  if (!e || e->bytes < bytes) {
+    if (capturing_) return ATTN_ERR_HIP;  // a capture can neither wait on the host nor allocate here
+    size_t want = bytes;
+    if (e) {
+      want = std::max(want, e->bytes + e->bytes / 2);
+      if (e->last_use && hipEventSynchronize(e->last_use) != hipSuccess) return ATTN_ERR_HIP;
+      if (hipFree(e->ptr) != hipSuccess) return ATTN_ERR_HIP;
+      e->ptr = nullptr;
+      e->bytes = 0;
+    } else {
+      g_ws.push_back(std::make_unique<StreamScratch>(StreamScratch{dev, stream, nullptr, 0, nullptr}));
+      e = g_ws.back().get();
+    }
+    constexpr size_t kGrain = (size_t)2 << 20;
+    want = (want + kGrain - 1) / kGrain * kGrain;
+    void* ptr = nullptr;
+    if (hipMalloc(&ptr, want) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return ATTN_ERR_OOM;
+    }
     e->ptr = ptr;
     e->bytes = want;
-  } else {
-    g_ws.push_back(StreamScratch{dev, stream, ptr, want});
   }
-  *out = ptr;
+  if (!capturing_ && e->last_use && hipStreamWaitEvent(stream, e->last_use, 0) != hipSuccess) return ATTN_ERR_HIP;
+  slot_ = e;
+  stream_ = stream;
+  *out = e->ptr;
   return ATTN_OK;
+}
+
+int ScratchCall::record() {
+  if (!slot_ || capturing_) return ATTN_OK;
+  if (!slot_->last_use && hipEventCreateWithFlags(&slot_->last_use, hipEventDisableTiming) != hipSuccess) {
+    slot_->last_use = nullptr;
+    return ATTN_ERR_HIP;
+  }
+  return hipEventRecord(slot_->last_use, stream_) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int release_stream_scratch() {
@@ -87,9 +127,14 @@ int release_stream_scratch() {
   int cur = 0;
   if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
   int status = ATTN_OK;
-  for (StreamScratch& s : g_ws) {
-    if (hipSetDevice(s.dev) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(s.ptr) != hipSuccess)
+  for (auto& s : g_ws) {
+    if (hipSetDevice(s->dev) != hipSuccess) {
       status = ATTN_ERR_HIP;
+      continue;
+    }
+    if (s->last_use && hipEventSynchronize(s->last_use) != hipSuccess) status = ATTN_ERR_HIP;
+    if (s->ptr && hipFree(s->ptr) != hipSuccess) status = ATTN_ERR_HIP;
+    if (s->last_use && hipEventDestroy(s->last_use) != hipSuccess) status = ATTN_ERR_HIP;
   }
   g_ws.clear();
   if (hipSetDevice(cur) != hipSuccess) status = ATTN_ERR_HIP;
@@ -366,15 +411,19 @@ int run(int flags, const void* q, const void* k, const void* v, void* o, float* 
       (void)hipGetLastError();
       return ATTN_ERR_HIP;
     }
-  } else if (parts > 0) {
-    const int sst = stream_scratch(stream, (size_t)plan.workspace_bytes, &ws);
+  }
+  ScratchCall call;  // held until the launches are enqueued (the allocating path only)
+  if (!noalloc && parts > 0) {
+    const int sst = call.acquire(stream, (size_t)plan.workspace_bytes, &ws);
     if (sst != ATTN_OK) return sst;
   }
   float* wsf = static_cast<float*>(ws);
   p.ws_acc = wsf;  // [parts][Dv] first: 16-byte aligned rows
   p.ws_m = wsf + parts * Dv;
   p.ws_l = p.ws_m + parts;
-  return launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
+  const int launched = launch_status(plan.path == 1 ? launch_prefill_bf16(p, stream) : launch_decode_bf16(p, stream));
+  const int recorded = call.record();
+  return launched != ATTN_OK ? launched : recorded;
 }
 
 }  // namespace
@@ -465,13 +514,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 
   // Scratch: delta and lse2 per row.
   void* ws = nullptr;
+  ScratchCall call;
   if (rows > 0) {
-    const int sst = stream_scratch(stream, (size_t)(rows * 2 * 4), &ws);
+    const int sst = call.acquire(stream, (size_t)(rows * 2 * 4), &ws);
     if (sst != ATTN_OK) return sst;
   }
   p.delta = static_cast<float*>(ws);
   p.lse2 = p.delta ? p.delta + rows : nullptr;
-  return launch_status(launch_bwd_bf16(p, stream));
+  const int launched = launch_status(launch_bwd_bf16(p, stream));
+  const int recorded = call.record();
+  return launched != ATTN_OK ? launched : recorded;
 }
 
 int attn_fwd_release_scratch(void) { return attn::release_stream_scratch(); }

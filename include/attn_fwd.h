@@ -34,15 +34,19 @@
  * alias the inputs.  Scratch for the split-KV passes (decode, and prefill
  * when its tiles are few) and for the backward is a library-owned device
  * buffer per (device, stream) the library has been called on: calls on one
- * stream run in stream order and share it, calls on different streams never
- * do.  A call that needs more than the stream's buffer holds waits for the
- * stream, then frees and reallocates it (at least 1.5x, rounded to 2 MiB);
- * no other call synchronises with the host, so calls can be queued ahead of
- * the GPU.  The buffers are kept until attn_fwd_release_scratch or process
- * exit.  The buffer is keyed by the stream handle: before a stream is
- * destroyed, its calls must have completed (as for any work on it).  Under
- * HIP graph capture, make one call of the same or larger size on the stream
- * first (a capture cannot wait for the stream), or use attn_fwd_noalloc.
+ * stream share it in stream order, calls on different streams never share
+ * one.  Each call makes its stream wait (on the GPU) for the buffer's
+ * previous call, so a new stream that reuses a destroyed stream's handle
+ * cannot overtake the old stream's work on it.  A call that needs more than
+ * the buffer holds waits on the host for the buffer's previous call, then
+ * frees and reallocates it (at least 1.5x, rounded to 2 MiB); no other call
+ * synchronises with the host, so calls can be queued ahead of the GPU.  The
+ * buffers are kept until attn_fwd_release_scratch or process exit.  Under
+ * HIP graph capture a call uses the capturing stream's buffer as it stands:
+ * make one call of the same or larger plan on that stream before capturing
+ * (a capture that would need a larger buffer returns ATTN_ERR_HIP), and do
+ * not run replays concurrently with other calls on that stream; or use
+ * attn_fwd_noalloc.
  *
  * Head widths: D and Dv up to 128 run on kernels sized for them; wider
  * heads run on 8-wave forms of the prefill kernel (decode with more than 16

@@ -105,3 +105,37 @@ def test_release_then_call_again(orc):
     assert _call(af.attn_fwd_ex, w, dev, b, st) == af.ATTN_OK
     torch.cuda.synchronize()
     _check(w, host, dev, b, orc, "after the release")
+
+
+def test_captured_call_replays_match_eager(orc):
+    """A split-KV decode call captured into a HIP graph (after one call of the
+    same size has sized the capturing stream's scratch) replays three times,
+    with eager calls on the same stream between replays; every replay is
+    bitwise the eager result."""
+    w = inputs.Workload("scratch_graph", 4, 16, 4, 1, 2600, 128, 128, seqlens=np.array([2600, 9, 1500, 0], np.int32))
+    assert af.attn_fwd_plan(*w.shape_tuple)["workspace_bytes"] > 0
+    host, dev = _dev(w)
+    s = torch.cuda.Stream()
+    eager, graphed = Outputs(w, w.dtype), Outputs(w, w.dtype)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        assert _call(af.attn_fwd_ex, w, dev, eager, s) == af.ATTN_OK  # sizes s's scratch
+    torch.cuda.synchronize()
+    _check(w, host, dev, eager, orc, "eager before capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = _call(af.attn_fwd_ex, w, dev, graphed, s)
+    assert st == af.ATTN_OK
+    for i in range(3):
+        graphed.o.fill_(float("nan"))
+        graphed.l.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+            other = Outputs(w, w.dtype)
+            torch.cuda.synchronize()
+            assert _call(af.attn_fwd_ex, w, dev, other, s) == af.ATTN_OK  # an eager call between replays
+        torch.cuda.synchronize()
+        say(f"[scratch] replay {i}")
+        assert torch.equal(graphed.o_raw, eager.o_raw) and torch.equal(graphed.l_raw, eager.l_raw), f"replay {i}"
+        assert torch.equal(other.o_raw, eager.o_raw) and torch.equal(other.l_raw, eager.l_raw), f"eager {i}"
