@@ -168,26 +168,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // get O = 0 and LSE = -inf, or an empty partial state, without loading Q.
   // The condition is uniform over the workgroup.
   if (jb0 >= jb1) {
-    if (wave_has_rows) {
+    if (!wave_has_rows) return;
+    if (p.n_split > 1) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (!row_ok[t]) continue;
-        if (p.n_split > 1) {
-          if (lead && g4 == 0) {
-            p.ws_m[part_slot(t)] = -INFINITY;
-            p.ws_l[part_slot(t)] = 0.f;
-          }
-        } else {
-          uint16_t* orow = static_cast<uint16_t*>(p.o) + row_index(t) * Dv_all + dv0;
-#pragma unroll
-          for (int j = 0; j < S::JV; ++j) {
-            const int dv = 16 * j + 4 * g4;
-            if (dv < Dv) *reinterpret_cast<ushort4*>(orow + dv) = ushort4{0, 0, 0, 0};
-          }
-          if (lead && g4 == 0) p.lse[row_index(t)] = -INFINITY;
+        if (row_ok[t] && lead && g4 == 0) {
+          p.ws_m[part_slot(t)] = -INFINITY;
+          p.ws_l[part_slot(t)] = 0.f;
         }
       }
+      return;
     }
+    // Zero rows written whole, 16 bytes per lane.
+    const int nrows = min(ROWS_W, tile.n_rows - rw0), chunks = Dv / 8;
+    for (int i = lane; i < nrows * chunks; i += 64) {
+      const int rr = i / chunks, r = rw0 + rr;
+      const int hh = r / Q;
+      const int64_t row = ((int64_t)b * p.Hq + tile.h_base + hh) * Q + (r - hh * Q);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.o) + row * Dv_all + dv0 + 8 * (i - rr * chunks)) = zero_u4();
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (row_ok[t] && lead && g4 == 0) p.lse[row_index(t)] = -INFINITY;
     return;
   }
 
@@ -534,27 +536,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     }
     return;
   }
+  // O = acc / l in the storage type, staged row-major in this wave's slice
+  // of the ring (every wave passed the last block's barrier and no load is
+  // in flight, so the ring is free; rows padded by 16 bytes so the 8-byte
+  // writes of 16 rows fall on distinct banks), then stored as whole rows,
+  // 16 bytes per lane.
+  constexpr int OSTRIDE = DVP + 8;  // elements per staged row
+  static_assert(NW * ROWS_W * OSTRIDE * 2 <= S::LDS, "O staging fits the ring");
+  uint16_t* ostage = reinterpret_cast<uint16_t*>(ring) + wave * ROWS_W * OSTRIDE;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float lt = group4_sum(l_run[t]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (row_ok[t]) {
-      const int64_t row = row_index(t);
-      uint16_t* orow = static_cast<uint16_t*>(p.o) + row * Dv_all + dv0;
 #pragma unroll
-      for (int j = 0; j < S::JV; ++j) {
-        const int dv = 16 * j + 4 * g4;
-        if (dv < Dv) {
-          ushort4 ov;
-          ov.x = E::cvt(acc[j][t][0] * inv);
-          ov.y = E::cvt(acc[j][t][1] * inv);
-          ov.z = E::cvt(acc[j][t][2] * inv);
-          ov.w = E::cvt(acc[j][t][3] * inv);
-          *reinterpret_cast<ushort4*>(orow + dv) = ov;
-        }
-      }
-      if (lead && g4 == 0) p.lse[row] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+    for (int j = 0; j < S::JV; ++j) {
+      ushort4 ov;
+      ov.x = E::cvt(acc[j][t][0] * inv);
+      ov.y = E::cvt(acc[j][t][1] * inv);
+      ov.z = E::cvt(acc[j][t][2] * inv);
+      ov.w = E::cvt(acc[j][t][3] * inv);
+      *reinterpret_cast<ushort4*>(ostage + (16 * t + l16) * OSTRIDE + 16 * j + 4 * g4) = ov;
     }
+    if (row_ok[t] && lead && g4 == 0)
+      p.lse[row_index(t)] = lt > 0.f ? (m_run[t] + __log2f(lt)) * 0.69314718055994530942f : -INFINITY;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int nrows = min(ROWS_W, tile.n_rows - rw0), chunks = Dv / 8;
+  for (int i = lane; i < nrows * chunks; i += 64) {
+    const int rr = i / chunks, c8 = 8 * (i - rr * chunks), r = rw0 + rr;
+    const int hh = r / Q;
+    const int64_t row = ((int64_t)b * p.Hq + tile.h_base + hh) * Q + (r - hh * Q);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.o) + row * Dv_all + dv0 + c8) =
+        *reinterpret_cast<const uint4*>(ostage + rr * OSTRIDE + c8);
   }
 }
 
