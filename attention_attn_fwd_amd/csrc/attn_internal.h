@@ -149,6 +149,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16-byte stores (non-temporal builtin)
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
 #define ATTN_LDS __attribute__((address_space(3)))
