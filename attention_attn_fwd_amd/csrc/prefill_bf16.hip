@@ -302,23 +302,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   // window edge or the sequence end: 0 for a legal key, -inf otherwise, so the
   // products leave -inf at every illegal key.  Key kb0 + 4*g4 + x (x = 16i +
   // r) is legal for query position pq iff lo <= x <= hi, with hi from
-  // causality and K_b and lo from the window: one unsigned compare against an
-  // immediate x per element.
+  // causality and K_b and lo from the window.  Which bound can bite anywhere
+  // in the wave is known per block (scalar): the upper one on the diagonal or
+  // at K_b, the lower one at a window edge; with one of them, one signed
+  // compare against an immediate x per element, with both one unsigned range
+  // compare (an empty range moves lo out of reach).
   auto mask_bias = [&](int kb0, f32x4 (&s)[KT][NT]) {
+    const bool need_lo = W > 0 && kb0 < pw_last - W + 1;
+    const bool need_hi = !(kb0 + BN - 1 <= pw_first && kb0 + BN <= Kb);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int rel = q_row[t] + delta - kb0 - 4 * g4;  // pq - (kb0 + 4*g4)
       const int hi = min(rel, Kb - kb0 - 4 * g4 - 1);
       const int lo = W > 0 ? max(rel - W + 1, 0) : 0;
-      const uint32_t span = (uint32_t)(hi - lo);
-      const bool none = hi < lo;
+      if (need_lo && need_hi) {
+        const bool none = hi < lo;
+        const uint32_t span = none ? 0u : (uint32_t)(hi - lo);
+        const int lo2 = none ? (1 << 30) : lo;
 #pragma unroll
-      for (int i = 0; i < KT; ++i) {
+        for (int i = 0; i < KT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool legal = !none & ((uint32_t)(16 * i + r - lo) <= span);
-          s[i][t][r] = legal ? 0.f : -INFINITY;
-        }
+          for (int r = 0; r < 4; ++r) s[i][t][r] = (uint32_t)(16 * i + r - lo2) <= span ? 0.f : -INFINITY;
+      } else if (need_hi) {
+#pragma unroll
+        for (int i = 0; i < KT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[i][t][r] = 16 * i + r <= hi ? 0.f : -INFINITY;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KT; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[i][t][r] = 16 * i + r >= lo ? 0.f : -INFINITY;
       }
     }
   };
