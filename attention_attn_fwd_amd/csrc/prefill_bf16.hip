@@ -242,12 +242,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
   const uint32_t lds0 = lds_offset(ring);
   // Block jb's loads; `page` holds its keys when the cache is paged (blocks
   // never straddle a page), read from the table a block ahead of its use.
+  // Contiguous cache: the (batch, kv-head) slices' addresses once per tile;
+  // a block's K/V start at a 32-bit byte offset into them.
+  const uint16_t* kslice = static_cast<const uint16_t*>(p.k) + ((int64_t)b * p.Hkv + kh) * p.K * D;
+  const uint16_t* vslice = static_cast<const uint16_t*>(p.v) + ((int64_t)b * p.Hkv + kh) * p.K * Dv_all;
   auto issue = [&](int jb, int stg, int page) {
     const int kb0 = jb * BN;
-    const KvSpan sp = kv_span_t<PAGED>(p, b, kh, kb0, page);
-    const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
-    const rsrc_t rk = slice_rsrc(sp.k, rows_left * D * 2);
-    const rsrc_t rv = slice_rsrc(sp.v, rows_left * Dv_all * 2);
+    rsrc_t rk, rv;
+    if constexpr (PAGED) {
+      const KvSpan sp = kv_span_t<PAGED>(p, b, kh, kb0, page);
+      const uint32_t rows_left = (uint32_t)min(Kb - kb0, sp.rows);
+      rk = slice_rsrc(sp.k, rows_left * D * 2);
+      rv = slice_rsrc(sp.v, rows_left * Dv_all * 2);
+    } else {
+      (void)page;
+      const uint32_t rows_left = (uint32_t)(Kb - kb0);
+      rk = slice_rsrc(reinterpret_cast<const char*>(kslice) + (uint32_t)kb0 * (uint32_t)(D * 2), rows_left * D * 2);
+      rv = slice_rsrc(reinterpret_cast<const char*>(vslice) + (uint32_t)kb0 * (uint32_t)(Dv_all * 2),
+                      rows_left * Dv_all * 2);
+    }
     const uint32_t kbase = lds0 + stg * S::K_TILE + wave * 1024;
     const uint32_t vbase = lds0 + S::V_BASE + stg * S::V_TILE + wave * 1024;
 #pragma unroll
@@ -277,16 +290,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
               (l16 & 1) * 8;
   }
 
-  // Whether any row of this wave has a legal key in block jb / every key of
-  // block jb is legal for every row of this wave (scalar).
-  auto wave_sees = [&](int jb) {
-    const int kb0 = jb * BN;
-    return wave_has_rows && kb0 <= pw_last && kb0 < Kb && !(W > 0 && kb0 + BN - 1 < pw_first - W + 1);
-  };
-  auto wave_full = [&](int jb) {
-    const int kb0 = jb * BN;
-    return (kb0 + BN - 1 <= pw_first) && (kb0 + BN <= Kb) && (W <= 0 || kb0 >= pw_last - W + 1);
-  };
+  // The blocks in which some row of this wave has a legal key, [see_lo,
+  // see_hi], and those in which every key is legal for every row of the
+  // wave, [full_lo, full_hi] (scalar, once per tile): a block is seen iff
+  // kb0 <= pw_last, kb0 < K_b and (no window or kb0 + BN - 1 >= pw_first -
+  // W + 1); full iff kb0 + BN - 1 <= pw_first, kb0 + BN <= K_b and (no
+  // window or kb0 >= pw_last - W + 1).  BN is a power of two, so the
+  // floor / ceiling divisions are arithmetic shifts for either sign.
+  constexpr int LG = BN == 64 ? 6 : 5;
+  static_assert((1 << LG) == BN, "block size");
+  auto fdiv = [](int a) { return a >> LG; };
+  auto cdiv = [](int a) { return (a + BN - 1) >> LG; };
+  const int see_hi = wave_has_rows ? min(fdiv(pw_last), fdiv(Kb - 1)) : -1;
+  const int see_lo = W > 0 ? cdiv(pw_first - W + 2 - BN) : 0;
+  const int full_hi = min(fdiv(pw_first - BN + 1), fdiv(Kb - BN));
+  const int full_lo = W > 0 ? cdiv(pw_last - W + 1) : 0;
 
   float m_run[NT], l_run[NT];
   f32x4 acc[S::JV][NT];
@@ -506,7 +524,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(Params p)
     const int pg = paged ? page_settle(pg_next) : 0;
     if (jb + 1 < jb1) issue(jb + 1, decltype(stg_tag)::value ^ 1, pg);
     if (paged) pg_next = page_fetch(jb + 2);
-    if (wave_sees(jb)) body(jb, stg_tag, wave_full(jb));
+    if (jb >= see_lo && jb <= see_hi) body(jb, stg_tag, jb >= full_lo && jb <= full_hi);
     // Block jb + 1 has landed for every wave, and every wave is done with
     // the stage of block jb, which the next block's loads overwrite.
     wait_vmcnt<0>();
