@@ -46,7 +46,16 @@ def _compile(out, defines=()):
     return out
 
 
+SANITIZE_MAIN = os.path.join(HERE, "sanitize_main.c")
+
+
 def build() -> str:
+    """The oracle library, and a compile-and-link check of the sanitizer driver
+    (tests/test_oracle_sanitized.py builds and runs it under ASan/UBSan)."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        subprocess.run(["gcc", "-std=c11", "-O1", "-fopenmp", "-Wall", "-Wextra", "-o", os.path.join(d, "driver"),
+                        SRC, SANITIZE_MAIN, "-lm"], check=True)
     return _compile(LIB)
 
 
